@@ -1,0 +1,169 @@
+/*
+ * mla.h -- C ABI of libmla.so: multi-head latent attention (MLA) over the
+ * latent KV cache, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources named by page title and section):
+ *   "Teardown: DeepSeek-V3", section 4 "Multi-head latent attention":
+ *     per token the cache holds the content latent c (d_c = 512) and one
+ *     rotary key k_R (d_r = 64) shared by all heads; per head h the content
+ *     key is k_C = W_UK c (d_h = 128), the value is v = W_UV c (d_v = 128);
+ *     query [q_C; q_R] and key [k_C; k_R] are scored with scale
+ *     1/sqrt(128 + 64); W_UK folds into the query at inference.
+ *   "DeepSeek-V3" (llm-vis explorer), boxes "KV latent compression" (cache
+ *     row = latent then rotary key; q^T (W_uk c) = (W_uk^T q)^T c; the value
+ *     up-projection folds into the output side) and "Scaled dot-product
+ *     attention" (softmax(q k^T * scale) v, causal mask, online
+ *     renormalisation over key blocks).
+ *
+ * Decode runs in the absorbed form:
+ *   mla_absorb_q      q_lat[m,h,:] = q_C[m,h,:] . W_UK[h]            (512 wide)
+ *   mla_decode_paged  per split s of each sequence's pages:
+ *                     s_t = (q_lat . c_t + q_R . k_R,t) * scale,
+ *                     o_s = sum_t softmax(s)_t c_t,  lse_s = ln sum_t e^{s_t}
+ *   mla_combine       o_lat = sum_s e^{lse_s - lse} o_s,  lse = ln sum_s e^{lse_s},
+ *                     out[m,h,:] = o_lat . W_UV[h]                   (128 wide)
+ * Prefill runs in the un-absorbed form (keys and values rebuilt per head).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; each call only enqueues
+ *     kernels on `stream` (a hipStream_t passed as void*; NULL = null stream)
+ *     and returns.
+ *   - Tensors are dense, row-major, contiguous.  bf16 values are passed as
+ *     uint16_t bit patterns; fp32 as float; indices as int32_t.
+ *   - Weight index order: w_uk is [H, d_h, d_c] with w_uk[h,i,j] multiplying
+ *     c[j] into k_C[i]; w_uv is [H, d_c, d_v] with w_uv[h,j,d] multiplying
+ *     c[j] into v[d].
+ *   - Cache: kv_cache is [num_blocks, block_size, d_c + d_r]; a row is c then
+ *     k_R.  block_table[b, p] names the block holding tokens
+ *     [p*block_size, (p+1)*block_size) of sequence b.
+ *   - seq_lens[b] = L_b counts every cached token of sequence b INCLUDING the
+ *     Tq (or T) query tokens, which are already in the cache.  Query i of a
+ *     sequence sits at position L_b - Tq + i and sees tokens 0 .. L_b - Tq + i.
+ *   - Supported shapes: H = 128, d_c = 512, d_r = 64, d_h = d_v = 128,
+ *     block_size = 64, 1 <= Tq <= 2 for decode.  Other values return
+ *     MLA_ERR_UNSUPPORTED.  NULL pointers, non-positive sizes, a too-small
+ *     workspace or num_splits outside [1, MLA_MAX_SPLITS] return
+ *     MLA_ERR_INVALID_ARG.  A HIP launch error returns MLA_ERR_HIP.
+ *   - Device-resident metadata (seq_lens, block_table) is NOT validated (that
+ *     would need a synchronisation).  Preconditions: Tq <= L_b <=
+ *     max_blocks_per_seq * block_size; 0 <= block_table[b,p] < num_blocks for
+ *     p < ceil(L_b / block_size); no block shared between sequences.  Entries
+ *     past a sequence's last block, rows past L_b in its last block and unused
+ *     blocks may hold anything (NaN included): they never reach an output.
+ *   - A query row that sees no key in a split gets o_s = 0 and lse_s = -inf.
+ *   - No mutable global state: calls on different streams may run
+ *     concurrently.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_HIP = 3
+};
+
+/* Largest num_splits accepted by mla_decode_paged / mla_combine. */
+#define MLA_MAX_SPLITS 256
+
+/* Static string describing a status code (never NULL). */
+const char* mla_strerror(int status);
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int mla_version(void);
+
+/*
+ * q-absorption ("KV latent compression": q^T (W_uk c) = (W_uk^T q)^T c):
+ *   q_lat[m, h, j] = sum_i q_c[m, h, i] * w_uk[h, i, j]     (fp32 accumulate)
+ * q_c   bf16 [M, H, d_h]   (M = B * Tq query rows)
+ * w_uk  bf16 [H, d_h, d_c]
+ * q_lat bf16 [M, H, d_c]   output, rounded to nearest even
+ * M may be any value in [1, 65536].
+ */
+int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat,
+                 int M, int H, int d_h, int d_c, void* stream);
+
+/*
+ * Split-KV flash decode over the paged latent cache (steps "scores", "online
+ * softmax", "causal mask" and the per-split partials of the absorbed form).
+ * q_lat  bf16 [B, Tq, H, d_c]   from mla_absorb_q
+ * q_r    bf16 [B, Tq, H, d_r]   rotary part of the query, already rotated
+ * kv_cache, block_table, seq_lens as described above
+ * softmax_scale: score scale (1/sqrt(192) for DeepSeek-V3's dims)
+ * num_splits S: each sequence's ceil(L_b / block_size) blocks are cut into S
+ *   contiguous ranges of ceil(blocks / S) blocks (trailing ranges may be empty)
+ * part_o   fp32 [S, B, Tq, H, d_c]  out: o_s, normalised within its split
+ * part_lse fp32 [S, B, Tq, H]       out: ln sum_{t in split} e^{s_t}
+ */
+int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
+                     const uint16_t* kv_cache, const int32_t* block_table,
+                     const int32_t* seq_lens,
+                     int B, int Tq, int H, int d_c, int d_r,
+                     int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int num_splits,
+                     float* part_o, float* part_lse, void* stream);
+
+/*
+ * Log-sum-exp merge of the splits, then the W_UV up-projection.
+ * part_o, part_lse as written by mla_decode_paged (M = B * Tq rows)
+ * w_uv    bf16 [H, d_c, d_v]
+ * out     bf16 [M, H, d_v]   out
+ * lse_out fp32 [M, H] or NULL: ln sum over all splits (natural log)
+ * A row whose splits are all empty gets out = 0 and lse = -inf.
+ */
+int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv,
+                uint16_t* out, float* lse_out,
+                int M, int H, int d_c, int d_v, int num_splits, void* stream);
+
+/*
+ * Causal prefill in the un-absorbed form: per head, keys [W_UK c; k_R]
+ * (192 wide) and values W_UV c (128 wide) are rebuilt from the cache into
+ * `workspace`, then softmax(q k^T * scale) v runs with the causal mask.
+ * q_c  bf16 [B, T, H, d_h], q_r bf16 [B, T, H, d_r]: queries of the LAST T
+ *      positions of each sequence (positions L_b - T .. L_b - 1)
+ * w_uk, w_uv as above; out bf16 [B, T, H, d_v]
+ * workspace: device scratch of at least
+ *      mla_prefill_workspace_bytes(B, max_blocks_per_seq, block_size, H, d_h, d_v)
+ *      bytes, 256-byte aligned.
+ */
+int mla_prefill(const uint16_t* q_c, const uint16_t* q_r,
+                const uint16_t* kv_cache, const int32_t* block_table,
+                const int32_t* seq_lens,
+                const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* out,
+                void* workspace, size_t workspace_bytes,
+                int B, int T, int H, int d_c, int d_r, int d_h, int d_v,
+                int num_blocks, int block_size, int max_blocks_per_seq,
+                float softmax_scale, void* stream);
+
+/* Bytes of part_o plus part_lse for one decode step (two separate buffers). */
+size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits);
+size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits);
+
+/* Workspace bytes mla_prefill needs. */
+size_t mla_prefill_workspace_bytes(int B, int max_blocks_per_seq, int block_size,
+                                   int H, int d_h, int d_v);
+
+/*
+ * Suggested num_splits for a decode step: enough work-groups (one per
+ * sequence, split and group of 128 query rows) to cover `num_cus` compute
+ * units about once, never more splits than the longest sequence has blocks,
+ * and at most MLA_MAX_SPLITS.  Host-only arithmetic; returns 0 on invalid
+ * arguments.
+ */
+int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size,
+                          int num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

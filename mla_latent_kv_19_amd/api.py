@@ -1,0 +1,237 @@
+"""Thin torch binding over libmla.so.
+
+Every function here only checks shapes, dtypes and devices, then passes raw
+device pointers and the current HIP stream to the C ABI (include/mla.h).  All
+arithmetic runs in the library's HIP kernels; nothing here computes, and there
+is no fallback: if the library is missing or a call fails, an exception is
+raised.
+
+bf16 tensors are torch.bfloat16 (bit-identical to the ABI's uint16 patterns).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+_lib = None
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
+MLA_MAX_SPLITS = 256
+
+# Shapes the kernels are written for.
+H, D_C, D_R, D_H, D_V, BLOCK = 128, 512, 64, 128, 128, 64
+
+EXPORTED = (
+    "mla_strerror", "mla_version", "mla_absorb_q", "mla_decode_paged", "mla_combine",
+    "mla_prefill", "mla_decode_part_o_bytes", "mla_decode_part_lse_bytes",
+    "mla_prefill_workspace_bytes", "mla_decode_num_splits",
+)
+
+
+class MLAError(RuntimeError):
+    """A non-zero status from libmla.so."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {strerror(status)}")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load():
+    """Load libmla.so (once) and declare the ABI's argument types."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m mla_latent_kv_19_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mla_strerror.argtypes, lib.mla_strerror.restype = [I], ctypes.c_char_p
+    lib.mla_version.argtypes, lib.mla_version.restype = [], I
+    lib.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, P]
+    lib.mla_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, P]
+    lib.mla_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.mla_prefill.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, I, F, P]
+    for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill"):
+        getattr(lib, fn).restype = I
+    lib.mla_decode_part_o_bytes.argtypes, lib.mla_decode_part_o_bytes.restype = [I, I, I, I, I], Z
+    lib.mla_decode_part_lse_bytes.argtypes, lib.mla_decode_part_lse_bytes.restype = [I, I, I, I], Z
+    lib.mla_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.mla_prefill_workspace_bytes.restype = Z
+    lib.mla_decode_num_splits.argtypes, lib.mla_decode_num_splits.restype = [I, I, I, I, I, I], I
+    _lib = lib
+    return lib
+
+
+def strerror(status):
+    return load().mla_strerror(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != MLA_OK:
+        raise MLAError(fn, status)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {devs}")
+    return devs.pop()
+
+
+def num_splits(batch, tq, max_seq_len, num_cus=None):
+    """Split count that covers the GPU's compute units about once."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    s = load().mla_decode_num_splits(batch, tq, H, max_seq_len, BLOCK, num_cus)
+    if s <= 0:
+        raise ValueError("invalid arguments to mla_decode_num_splits")
+    return s
+
+
+def absorb_q(q_c, w_uk, out=None):
+    """q_lat[m, h, :] = q_c[m, h, :] @ w_uk[h]; q_c [..., H, 128] -> [..., H, 512] bf16."""
+    lead = q_c.shape[:-2]
+    m = 1
+    for d in lead:
+        m *= d
+    _need(q_c, "q_c", torch.bfloat16, (*lead, H, D_H))
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_H, D_C))
+    if out is None:
+        out = torch.empty((*lead, H, D_C), dtype=torch.bfloat16, device=q_c.device)
+    _need(out, "out", torch.bfloat16, (*lead, H, D_C))
+    dev = _same_device(q_c, w_uk, out)
+    _check("mla_absorb_q", load().mla_absorb_q(_ptr(q_c), _ptr(w_uk), _ptr(out), m, H, D_H, D_C,
+                                                _stream(dev)))
+    return out
+
+
+def decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, softmax_scale, splits,
+                 part_o=None, part_lse=None):
+    """Split-KV decode; returns (part_o [S,B,Tq,H,512] fp32, part_lse [S,B,Tq,H] fp32)."""
+    b, tq = q_lat.shape[0], q_lat.shape[1]
+    _need(q_lat, "q_lat", torch.bfloat16, (b, tq, H, D_C))
+    _need(q_r, "q_r", torch.bfloat16, (b, tq, H, D_R))
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (BLOCK, D_C + D_R):
+        raise ValueError(f"kv_cache must be [num_blocks, {BLOCK}, {D_C + D_R}]")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, (b,))
+    if part_o is None:
+        part_o = torch.empty((splits, b, tq, H, D_C), dtype=torch.float32, device=q_lat.device)
+    if part_lse is None:
+        part_lse = torch.empty((splits, b, tq, H), dtype=torch.float32, device=q_lat.device)
+    _need(part_o, "part_o", torch.float32, (splits, b, tq, H, D_C))
+    _need(part_lse, "part_lse", torch.float32, (splits, b, tq, H))
+    dev = _same_device(q_lat, q_r, kv_cache, block_table, seq_lens, part_o, part_lse)
+    _check("mla_decode_paged", load().mla_decode_paged(
+        _ptr(q_lat), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+        b, tq, H, D_C, D_R, kv_cache.shape[0], BLOCK, block_table.shape[1],
+        ctypes.c_float(softmax_scale), splits, _ptr(part_o), _ptr(part_lse), _stream(dev)))
+    return part_o, part_lse
+
+
+def combine(part_o, part_lse, w_uv, out=None, lse_out=None, want_lse=False):
+    """Merge splits and apply W_UV; returns out [B,Tq,H,128] bf16 (and lse [B,Tq,H] fp32)."""
+    s, b, tq = part_o.shape[0], part_o.shape[1], part_o.shape[2]
+    _need(part_o, "part_o", torch.float32, (s, b, tq, H, D_C))
+    _need(part_lse, "part_lse", torch.float32, (s, b, tq, H))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    if out is None:
+        out = torch.empty((b, tq, H, D_V), dtype=torch.bfloat16, device=part_o.device)
+    _need(out, "out", torch.bfloat16, (b, tq, H, D_V))
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((b, tq, H), dtype=torch.float32, device=part_o.device)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (b, tq, H))
+    dev = _same_device(part_o, part_lse, w_uv, out, lse_out)
+    _check("mla_combine", load().mla_combine(
+        _ptr(part_o), _ptr(part_lse), _ptr(w_uv), _ptr(out), _ptr(lse_out),
+        b * tq, H, D_C, D_V, s, _stream(dev)))
+    return (out, lse_out) if lse_out is not None else out
+
+
+def decode_step(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale,
+                splits=None, max_seq_len=None, want_lse=False, workspace=None):
+    """One full decode step: absorb -> split-KV attention -> combine + W_UV.
+
+    q_c [B, Tq, H, 128], q_r [B, Tq, H, 64] bf16.  ``max_seq_len`` (a host
+    int) picks the split count when ``splits`` is not given; it avoids reading
+    seq_lens back from the device.  ``workspace`` may hold preallocated
+    (q_lat, part_o, part_lse) tensors.
+    """
+    b, tq = q_c.shape[0], q_c.shape[1]
+    if splits is None:
+        if max_seq_len is None:
+            max_seq_len = block_table.shape[1] * BLOCK
+        splits = num_splits(b, tq, max_seq_len)
+    if workspace is None:
+        q_lat = absorb_q(q_c, w_uk)
+        part_o = part_lse = None
+    else:
+        q_lat, part_o, part_lse = workspace
+        absorb_q(q_c, w_uk, out=q_lat)
+    part_o, part_lse = decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, softmax_scale,
+                                    splits, part_o, part_lse)
+    return combine(part_o, part_lse, w_uv, want_lse=want_lse)
+
+
+def prefill_workspace_bytes(batch, max_blocks_per_seq):
+    return load().mla_prefill_workspace_bytes(batch, max_blocks_per_seq, BLOCK, H, D_H, D_V)
+
+
+def prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale,
+            out=None, workspace=None):
+    """Causal prefill over the cache; q for the last T positions of each sequence."""
+    b, t = q_c.shape[0], q_c.shape[1]
+    _need(q_c, "q_c", torch.bfloat16, (b, t, H, D_H))
+    _need(q_r, "q_r", torch.bfloat16, (b, t, H, D_R))
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, (b,))
+    _need(w_uk, "w_uk", torch.bfloat16, (H, D_H, D_C))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    if out is None:
+        out = torch.empty((b, t, H, D_V), dtype=torch.bfloat16, device=q_c.device)
+    _need(out, "out", torch.bfloat16, (b, t, H, D_V))
+    nbytes = prefill_workspace_bytes(b, block_table.shape[1])
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q_c.device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"prefill workspace needs {nbytes} bytes")
+    dev = _same_device(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, out, workspace)
+    _check("mla_prefill", load().mla_prefill(
+        _ptr(q_c), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+        _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),
+        b, t, H, D_C, D_R, D_H, D_V, kv_cache.shape[0], BLOCK, block_table.shape[1],
+        ctypes.c_float(softmax_scale), _stream(dev)))
+    return out

@@ -1,0 +1,147 @@
+// Host side of the C ABI declared in include/mla.h: argument checks, launch
+// geometry and status mapping.  Kernels live in the .hip files; this file
+// only validates and dispatches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "mla.h"
+
+extern "C" hipError_t mla_launch_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat,
+                                          int M, hipStream_t stream);
+extern "C" hipError_t mla_launch_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
+                                              const uint16_t* kv, const int32_t* block_table,
+                                              const int32_t* seq_lens, int B, int Tq, int max_blocks,
+                                              float softmax_scale, int num_splits, float* part_o,
+                                              float* part_lse, hipStream_t stream);
+extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_lse,
+                                         const uint16_t* w_uv, uint16_t* out, float* lse_out, int M,
+                                         int S, hipStream_t stream);
+extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_r,
+                                         const uint16_t* kv, const int32_t* block_table,
+                                         const int32_t* seq_lens, const uint16_t* w_uk,
+                                         const uint16_t* w_uv, uint16_t* out, void* workspace,
+                                         int B, int T, int max_blocks, float softmax_scale,
+                                         hipStream_t stream);
+
+namespace {
+
+// The one shape family the kernels are written for (DeepSeek-V3's MLA dims).
+constexpr int kH = 128, kDC = 512, kDR = 64, kDH = 128, kDV = 128, kBlock = 64;
+constexpr int kMaxTq = 2;
+constexpr int kMaxRows = 65536;
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  if (e == hipErrorNotSupported) return MLA_ERR_UNSUPPORTED;
+  return MLA_ERR_HIP;
+}
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_strerror(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK: success";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive size or bad workspace/splits";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape outside H=128, d_c=512, d_r=64, d_h=d_v=128, block 64, Tq<=2";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    default: return "unknown mla status";
+  }
+}
+
+int mla_version(void) { return 100; }
+
+int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat, int M, int H, int d_h,
+                 int d_c, void* stream) {
+  if (!q_c || !w_uk || !q_lat || M <= 0 || H <= 0 || d_h <= 0 || d_c <= 0 || M > kMaxRows)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_h != kDH || d_c != kDC) return MLA_ERR_UNSUPPORTED;
+  return status_of(mla_launch_absorb_q(q_c, w_uk, q_lat, M, static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, int B, int Tq, int H,
+                     int d_c, int d_r, int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int num_splits, float* part_o, float* part_lse,
+                     void* stream) {
+  if (!q_lat || !q_r || !kv_cache || !block_table || !seq_lens || !part_o || !part_lse)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || Tq <= 0 || H <= 0 || d_c <= 0 || d_r <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || !finite_positive(softmax_scale) || num_splits < 1 ||
+      num_splits > MLA_MAX_SPLITS || (long)B * Tq > kMaxRows)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_c != kDC || d_r != kDR || block_size != kBlock || Tq > kMaxTq)
+    return MLA_ERR_UNSUPPORTED;
+  return status_of(mla_launch_decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq,
+                                           max_blocks_per_seq, softmax_scale, num_splits, part_o,
+                                           part_lse, static_cast<hipStream_t>(stream)));
+}
+
+int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv, uint16_t* out,
+                float* lse_out, int M, int H, int d_c, int d_v, int num_splits, void* stream) {
+  if (!part_o || !part_lse || !w_uv || !out || M <= 0 || H <= 0 || d_c <= 0 || d_v <= 0 ||
+      num_splits < 1 || num_splits > MLA_MAX_SPLITS || M > kMaxRows)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_c != kDC || d_v != kDV) return MLA_ERR_UNSUPPORTED;
+  return status_of(mla_launch_combine(part_o, part_lse, w_uv, out, lse_out, M, num_splits,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || d_c <= 0 || num_splits <= 0) return 0;
+  return (size_t)num_splits * B * Tq * H * d_c * sizeof(float);
+}
+
+size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || num_splits <= 0) return 0;
+  return (size_t)num_splits * B * Tq * H * sizeof(float);
+}
+
+size_t mla_prefill_workspace_bytes(int B, int max_blocks_per_seq, int block_size, int H, int d_h,
+                                   int d_v) {
+  if (B <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 || H <= 0 || d_h <= 0 || d_v <= 0)
+    return 0;
+  // Rebuilt content keys and values for every cached position: bf16 [B, H, Lmax, d_h + d_v].
+  return (size_t)B * max_blocks_per_seq * block_size * H * (d_h + d_v) * 2;
+}
+
+int mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv_cache,
+                const int32_t* block_table, const int32_t* seq_lens, const uint16_t* w_uk,
+                const uint16_t* w_uv, uint16_t* out, void* workspace, size_t workspace_bytes, int B,
+                int T, int H, int d_c, int d_r, int d_h, int d_v, int num_blocks, int block_size,
+                int max_blocks_per_seq, float softmax_scale, void* stream) {
+  if (!q_c || !q_r || !kv_cache || !block_table || !seq_lens || !w_uk || !w_uv || !out ||
+      !workspace)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || H <= 0 || d_c <= 0 || d_r <= 0 || d_h <= 0 || d_v <= 0 ||
+      num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+      !finite_positive(softmax_scale) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_c != kDC || d_r != kDR || d_h != kDH || d_v != kDV || block_size != kBlock)
+    return MLA_ERR_UNSUPPORTED;
+  if ((long)T > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < mla_prefill_workspace_bytes(B, max_blocks_per_seq, block_size, H, d_h, d_v))
+    return MLA_ERR_INVALID_ARG;
+  return status_of(mla_launch_prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, out,
+                                      workspace, B, T, max_blocks_per_seq, softmax_scale,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size, int num_cus) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || max_seq_len <= 0 || block_size <= 0 || num_cus <= 0) return 0;
+  const long groups = (long)B * (((long)Tq * H + 127) / 128);    // work-groups per split
+  const long pages = (max_seq_len + block_size - 1) / block_size;
+  long s = (num_cus + groups - 1) / groups;
+  if (s > pages) s = pages;
+  if (s > MLA_MAX_SPLITS) s = MLA_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Log-sum-exp merge of the decode splits, then the W_UV up-projection.
+//
+// "DeepSeek-V3" (llm-vis explorer), box "Scaled dot-product attention": the
+// key blocks are renormalised online, which gives the same result as one
+// softmax; here that renormalisation is applied once across splits:
+//   lse = ln sum_s e^{lse_s},  o_lat = sum_s e^{lse_s - lse} o_s.
+// "Output projection" box / "Teardown: DeepSeek-V3" section 4: the value
+// up-projection v = W_UV c folds into the output side, so
+//   out[m, h, d] = sum_j o_lat[m, h, j] W_UV[h][j][d]      (512 -> 128)
+//
+// One work-group per (head, block of 32 query rows).  The merged o_lat rows are
+// kept in LDS as a bf16 hi/lo pair (o = hi + lo to about 16 bits), so the
+// bf16 MFMA product carries nearly fp32 accuracy of o_lat at twice the (tiny)
+// matrix work.  W_UV[h] is staged through LDS in 128-row slices and read with
+// transposed reads to form the 8-consecutive-j operand layout.
+#include "mla_common.h"
+
+namespace mla {
+
+constexpr int kCmbThreads = 256;
+constexpr int kOPitch = 512 + 8;     // bf16 per o_lat LDS row (1040 B)
+constexpr int kWPitch = 128 + 16;    // bf16 per W_UV LDS row (288 B)
+
+__global__ __launch_bounds__(kCmbThreads) void combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+    int M, int S) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cmb_smem[];
+  uint16_t* o_hi = reinterpret_cast<uint16_t*>(cmb_smem);             // [32][kOPitch]
+  uint16_t* o_lo = o_hi + 32 * kOPitch;                               // [32][kOPitch]
+  uint16_t* wt = o_lo + 32 * kOPitch;                                 // [128][kWPitch]
+  float* wts = reinterpret_cast<float*>(wt + 128 * kWPitch);          // [S][32]
+
+  const int h = blockIdx.x % 128;
+  const int m0 = (blockIdx.x / 128) * 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int wave = tid >> 6;
+  const size_t split_stride = (size_t)M * 128;   // rows of one split
+
+  // 1. Split weights per row.
+  if (tid < 32) {
+    const int m = m0 + tid;
+    float mx = -INFINITY;
+    if (m < M)
+      for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[s * split_stride + (size_t)m * 128 + h]);
+    float z = 0.f;
+    if (mx != -INFINITY)
+      for (int s = 0; s < S; ++s) {
+        const float w = __expf(part_lse[s * split_stride + (size_t)m * 128 + h] - mx);
+        wts[s * 32 + tid] = w;
+        z += w;
+      }
+    const float inv = (z > 0.f) ? 1.f / z : 0.f;
+    for (int s = 0; s < S; ++s) wts[s * 32 + tid] = (mx != -INFINITY) ? wts[s * 32 + tid] * inv : 0.f;
+    if (lse_out != nullptr && m < M)
+      lse_out[(size_t)m * 128 + h] = (mx != -INFINITY) ? mx + __logf(z) : -INFINITY;
+  }
+  __syncthreads();
+
+  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2k.
+  {
+    const int cq = tid & 127;
+    for (int r = tid >> 7; r < 32; r += 2) {
+      const int m = m0 + r;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m < M) {
+        const float* src = part_o + ((size_t)m * 128 + h) * 512 + 4 * cq;
+        for (int s = 0; s < S; ++s) {
+          const float w = wts[s * 32 + r];
+          if (w != 0.f) {
+            const float4 v = *reinterpret_cast<const float4*>(src + s * split_stride * 512);
+            o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
+          }
+        }
+      }
+      const float ov[4] = {o.x, o.y, o.z, o.w};
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)ov[e];
+        lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
+      *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
+    }
+  }
+
+  // 3. out[32 rows x 128] = o_lat . W_UV[h]; wave w owns columns 32w .. 32w+31.
+  const int q16 = lane & 15;
+  const int colhalf = (lane >> 4) & 1;
+  const lds_u8* trb = to_lds(wt) +
+                      ((8 * half + (q16 >> 2)) * kWPitch + 32 * wave + 16 * colhalf + 4 * (q16 & 3)) * 2;
+  const lds_u8* ahb = to_lds(o_hi) + (l32 * kOPitch + 8 * half) * 2;
+  const lds_u8* alb = to_lds(o_lo) + (l32 * kOPitch + 8 * half) * 2;
+  f32x16 acc = {};
+  const uint16_t* wsrc = w_uv + (size_t)h * 512 * 128;
+  for (int jc = 0; jc < 4; ++jc) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int chunk = k * kCmbThreads + tid;   // 128 rows x 16 chunks
+      const int j = chunk >> 4, c = chunk & 15;
+      *reinterpret_cast<uint4*>(&wt[j * kWPitch + c * 8]) =
+          *reinterpret_cast<const uint4*>(wsrc + (size_t)(jc * 128 + j) * 128 + c * 8);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x4 blo = ld_lds_tr(trb + (16 * ks) * kWPitch * 2);
+      const bf16x4 bhi = ld_lds_tr(trb + (16 * ks + 4) * kWPitch * 2);
+      const bf16x8 bw = cat(blo, bhi);
+      const int koff = (jc * 128 + 16 * ks) * 2;
+      acc = mfma32(ld_lds_bf16x8(ahb + koff), bw, acc);
+      acc = mfma32(ld_lds_bf16x8(alb + koff), bw, acc);
+    }
+  }
+  // acc[r]: row m0 + 8*(r/4) + 4*half + r%4, column 32*wave + l32.
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (m < M) {
+      const __bf16 v = (__bf16)acc[r];
+      out[((size_t)m * 128 + h) * 128 + 32 * wave + l32] = __builtin_bit_cast(uint16_t, v);
+    }
+  }
+}
+
+size_t combine_lds_bytes(int S) {
+  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)S * 32 * 4;
+}
+
+}  // namespace mla
+
+extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_lse,
+                                         const uint16_t* w_uv, uint16_t* out, float* lse_out, int M,
+                                         int S, hipStream_t stream) {
+  const size_t lds = mla::combine_lds_bytes(S);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&mla::combine_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::combine_lds_bytes(256));
+  if (attr != hipSuccess) return attr;
+  const int grid = 128 * ((M + 31) / 32);
+  void* args[] = {&part_o, &part_lse, &w_uv, &out, &lse_out, &M, &S};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mla::combine_kernel), dim3(grid),
+                         dim3(mla::kCmbThreads), args, lds, stream);
+}

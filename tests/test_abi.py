@@ -1,0 +1,128 @@
+"""CPU checks of the C ABI: the library loads, exports what include/mla.h
+declares, and rejects bad arguments on the host without touching a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+api = pytest.importorskip("mla_latent_kv_19_amd.api")
+
+
+def _lib():
+    if not os.path.exists(api.library_path()):
+        pytest.skip("libmla.so not built")
+    return api.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    names = _declared_functions()
+    assert names
+    for fn in names:
+        assert hasattr(lib, fn), f"{fn} declared in mla.h but not exported"
+    assert set(names) <= set(api.EXPORTED) | {"mla_decode_paged_noalloc"}
+
+
+def test_strerror_and_version():
+    lib = _lib()
+    for code in range(4):
+        assert lib.mla_strerror(code)
+    assert b"unknown" in lib.mla_strerror(99)
+    assert lib.mla_version() >= 100
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
+
+
+def test_absorb_q_argument_errors():
+    lib = _lib()
+    assert lib.mla_absorb_q(NULL, FAKE, FAKE, 4, 128, 128, 512, NULL) == api.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 0, 128, 128, 512, NULL) == api.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 64, 128, 512, NULL) == api.MLA_ERR_UNSUPPORTED
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 128, 128, 256, NULL) == api.MLA_ERR_UNSUPPORTED
+
+
+def _decode(lib, **kw):
+    a = dict(q_lat=FAKE, q_r=FAKE, kv=FAKE, table=FAKE, lens=FAKE, B=2, Tq=1, H=128, d_c=512,
+             d_r=64, num_blocks=10, block_size=64, max_blocks=5, scale=0.07, splits=2,
+             part_o=FAKE, part_lse=FAKE)
+    a.update(kw)
+    return lib.mla_decode_paged(a["q_lat"], a["q_r"], a["kv"], a["table"], a["lens"], a["B"],
+                                a["Tq"], a["H"], a["d_c"], a["d_r"], a["num_blocks"],
+                                a["block_size"], a["max_blocks"], ctypes.c_float(a["scale"]),
+                                a["splits"], a["part_o"], a["part_lse"], NULL)
+
+
+def test_decode_argument_errors():
+    lib = _lib()
+    E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
+    assert _decode(lib, kv=NULL) == E
+    assert _decode(lib, part_lse=NULL) == E
+    assert _decode(lib, B=0) == E
+    assert _decode(lib, splits=0) == E
+    assert _decode(lib, splits=api.MLA_MAX_SPLITS + 1) == E
+    assert _decode(lib, scale=0.0) == E
+    assert _decode(lib, scale=float("nan")) == E
+    assert _decode(lib, H=64) == U
+    assert _decode(lib, block_size=16) == U
+    assert _decode(lib, Tq=3) == U
+    assert _decode(lib, d_r=32) == U
+
+
+def test_combine_argument_errors():
+    lib = _lib()
+    E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
+    assert lib.mla_combine(NULL, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 128, 2, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 128, 0, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 64, 2, NULL) == U
+
+
+def test_prefill_argument_errors():
+    lib = _lib()
+    E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
+    aligned = ctypes.c_void_p(0x10000)
+    need = lib.mla_prefill_workspace_bytes(1, 64, 64, 128, 128, 128)
+    assert need == 64 * 64 * 128 * 256 * 2
+
+    def call(ws=aligned, ws_bytes=need, T=4096, H=128, max_blocks=64):
+        return lib.mla_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                               1, T, H, 512, 64, 128, 128, 70, 64, max_blocks,
+                               ctypes.c_float(0.07), NULL)
+    assert call(ws=NULL) == E
+    assert call(ws=ctypes.c_void_p(0x10010)) == E          # not 256-byte aligned
+    assert call(ws_bytes=need - 1) == E
+    assert call(T=64 * 64 + 1) == E                          # more queries than cache slots
+    assert call(H=96) == U
+
+
+def test_workspace_sizes_and_split_heuristic():
+    lib = _lib()
+    assert lib.mla_decode_part_o_bytes(64, 1, 128, 512, 4) == 4 * 64 * 128 * 512 * 4
+    assert lib.mla_decode_part_lse_bytes(64, 1, 128, 4) == 4 * 64 * 128 * 4
+    assert lib.mla_decode_part_o_bytes(0, 1, 128, 512, 4) == 0
+    # 64 sequences on 256 compute units: 4 splits; 8 long sequences: 32 splits.
+    assert lib.mla_decode_num_splits(64, 1, 128, 32768, 64, 256) == 4
+    assert lib.mla_decode_num_splits(8, 1, 128, 163840, 64, 256) == 32
+    assert lib.mla_decode_num_splits(64, 2, 128, 8192, 64, 256) == 2
+    # Never more splits than blocks of the longest sequence.
+    assert lib.mla_decode_num_splits(1, 1, 128, 1024, 64, 256) == 16
+    assert lib.mla_decode_num_splits(1, 1, 128, 1, 64, 256) == 1
+    assert lib.mla_decode_num_splits(0, 1, 128, 1, 64, 256) == 0
