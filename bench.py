@@ -1,0 +1,231 @@
+"""Benchmark of the MLA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one full decode pass over one batch: q-absorption (W_UK folded into
+the query), split-KV attention over the paged latent cache, log-sum-exp
+combine and the W_UV up-projection.  Inputs are seeded synthetic data with
+the shapes of the pages' model (128 heads, latent 512 + rotary 64, content
+head 128) and are resident in HBM before timing starts.
+
+Prints one JSON line: whole-job throughput in KV-tokens/s, the dominant
+kernel's roofline position (algorithmic bytes / measured launch time against
+the 8 TB/s HBM peak), and the fp64 CPU oracle timed on a bounded sample on
+this host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-tokens/s and TFLOP/s (+% HBM/MFMA roofline), B=64 ctx 32K, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak
+ROW_BYTES = 576 * 2            # one cached token: latent 512 + rotary key 64, bf16
+FLOP_PER_TOKEN_QUERY = 128 * 2 * (576 + 512)   # scores + value product, all heads
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_headline_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for name in ("decode.hip", "mla_common.h"):
+        with open(os.path.join(ROOT, "mla_latent_kv_19_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_algorithmic):
+    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != decode_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp_meta, budget_s):
+    """The fp64 oracle (un-absorbed form) on a bounded sample of the workload.
+
+    The sample is whole sequences (all heads) regenerated from their seeded
+    streams, as many as fit the time budget (at least one), timed with
+    perf_counter around the oracle calls only.
+    """
+    import oracle
+    from mla_latent_kv_19_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q_c, q_r = synth.queries_for(wl)
+    w_uk, w_uv = (synth.bf16_bits_to_f64(w) for w in synth.weights_for(wl))
+    spent, tokens, n_seq = 0.0, 0, 0
+    for b in range(wl.batch):
+        L = int(inp_meta["seq_lens"][b])
+        rows = synth.bf16_bits_to_f64(synth.sequence_rows(wl, b, L))
+        n_blk = (L + wl.block_size - 1) // wl.block_size
+        kv = np.zeros((n_blk * wl.block_size, rows.shape[1]))
+        kv[:L] = rows
+        kv = kv.reshape(n_blk, wl.block_size, rows.shape[1])
+        table = np.arange(n_blk, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        oracle.decode(synth.bf16_bits_to_f64(q_c[b:b + 1]), synth.bf16_bits_to_f64(q_r[b:b + 1]),
+                      kv, table, np.array([L], dtype=np.int32), w_uk, w_uv, wl.scale)
+        spent += time.perf_counter() - t0
+        tokens += L
+        n_seq += 1
+        if spent * (n_seq + 1) / n_seq > budget_s:
+            break
+    return {"value": tokens / spent, "unit": "KV-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of {wl.batch} sequences (all {wl.heads} heads, "
+                      f"{tokens} KV tokens), un-absorbed fp64 numpy oracle, {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode path has no multi-GPU component).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mla_latent_kv_19_amd import api, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    api.load()
+    wl = synth.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(wl)
+    gen_s = time.perf_counter() - t_gen
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q_c, q_r = dev(inp.q_c), dev(inp.q_r)
+    kv = dev(inp.kv_cache)
+    table = torch.from_numpy(inp.block_table).cuda()
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    w_uk, w_uv = dev(inp.w_uk), dev(inp.w_uv)
+    B, Tq = wl.batch, wl.tq
+    max_len = int(inp.seq_lens.max())
+    splits = args.splits or api.num_splits(B, Tq, max_len)
+    q_lat = torch.empty((B, Tq, 128, 512), dtype=torch.bfloat16, device="cuda")
+    part_o = torch.empty((splits, B, Tq, 128, 512), dtype=torch.float32, device="cuda")
+    part_lse = torch.empty((splits, B, Tq, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Tq, 128, 128), dtype=torch.bfloat16, device="cuda")
+    meta = {"seq_lens": inp.seq_lens}
+    kv_tokens = int(inp.seq_lens.astype(np.int64).sum())
+    del inp
+
+    def step():
+        api.absorb_q(q_c, w_uk, out=q_lat)
+        api.decode_paged(q_lat, q_r, kv, table, lens, wl.scale, splits, part_o, part_lse)
+        api.combine(part_o, part_lse, w_uv, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel launch durations, events on the stream the kernels run on.
+    def time_kernel(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    n_k = max(5, args.steps)
+    t_absorb = time_kernel(lambda: api.absorb_q(q_c, w_uk, out=q_lat), n_k)
+    t_decode = time_kernel(lambda: api.decode_paged(q_lat, q_r, kv, table, lens, wl.scale, splits,
+                                                    part_o, part_lse), n_k)
+    t_combine = time_kernel(lambda: api.combine(part_o, part_lse, w_uv, out=out), n_k)
+
+    kv_bytes = kv_tokens * ROW_BYTES
+    weight_bytes = 2 * 128 * 128 * 512 * 2
+    q_bytes = B * Tq * 128 * (128 + 64) * 2
+    out_bytes = B * Tq * 128 * 128 * 2
+    step_bytes = kv_bytes + weight_bytes + q_bytes + out_bytes
+    flops = kv_tokens * Tq * FLOP_PER_TOKEN_QUERY + 2 * B * Tq * 128 * 2 * 128 * 512
+    value = kv_tokens / (ms_step * 1e-3)
+    achieved = kv_bytes / (t_decode * 1e-3) / 1e9
+    traffic = measured_traffic(kv_bytes)
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "batch": B, "query_tokens": Tq,
+                   "seq_len": max_len, "heads": 128, "latent": 512, "rope": 64, "head_dim": 128,
+                   "block_size": 64, "splits": splits, "kv_tokens": kv_tokens},
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_mfma_frac": flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "kernels_ms": {"absorb_q": t_absorb, "decode_paged": t_decode, "combine": t_combine},
+        "roofline": {
+            "kernel": "decode_paged_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "mfma_tflops": kv_tokens * Tq * FLOP_PER_TOKEN_QUERY / (t_decode * 1e-3) / 1e12,
+        },
+        "wall_s": wall,
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, meta, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
