@@ -38,6 +38,9 @@ constexpr int kDecLdsBytes = 2 * kPageBytes;   // double buffer
 
 static_assert(kLoadsPerThread * 16 * kDecThreads == kPageBytes, "page must split evenly");
 
+// Lazy renormalisation threshold (log2 units): unnormalised weights stay <= 2^8.
+constexpr float kLazy = 8.f;
+
 // LDS placement of chunk c of token row t: the low three bits of the chunk
 // index are XORed with a per-row pattern so that both the 16-byte row reads of
 // the score product (8 rows, same chunk) and the transposed reads of the value
@@ -132,8 +135,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   f32x16 acc[16];
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-  float m_run = -INFINITY;   // running max of scores, log2 units
-  float l_run = 0.f;         // this lane's share of the running sum
+  float m_ref = -INFINITY;   // exponent reference (<= running max + 0), log2 units
+  float l_run = 0.f;         // this lane's share of sum 2^(x - m_ref)
 
   // Per-lane LDS offsets.
   // Score product: lane reads token (l32) of the slice, chunk 2kk + half.
@@ -152,14 +155,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
 
   for (int i = 0; i < count; ++i) {
     lds_u8* cur = smem + (i & 1) * kPageBytes;
-    if (i + 1 < count) {
+    // One barrier per page: after it, page i has landed for every wave and
+    // every wave has finished page i-1, whose buffer then takes page i+1.
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (i + 1 < count)
       issue_page(kv + (size_t)table[p0 + i + 1] * (kTok * kRowVals),
                  smem + ((i + 1) & 1) * kPageBytes, tid);
-      wait_vmcnt<kLoadsPerThread>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();
 
     const int pg = p0 + i;
     const int valid = L - pg * kTok;                // rows of this page inside the sequence
@@ -198,9 +200,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
         mx = fmaxf(mx, x[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      // Lazy renormalisation: the exponent reference m_ref only moves when the
+      // slice maximum exceeds it by more than kLazy (so p <= 2^kLazy); the
+      // accumulators are rescaled only then, and not at all on the first
+      // visible slice, when they are still zero.
+      const bool move = mx > m_ref + kLazy;
+      if (__any(move && m_ref != -INFINITY)) {
+        const float alpha = move ? fast_exp2(m_ref - mx) : 1.f;
         l_run *= alpha;
         agpr_scale_begin();
 #pragma unroll
@@ -209,8 +215,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
           for (int r = 0; r < 16; ++r) MLA_AGPR_SCALE(acc[cb][r], alpha);
         agpr_scale_end();
       }
-      m_run = m_new;
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      if (move) m_ref = mx;
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       bf16x8 pb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -231,7 +237,6 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
         }
       }
     }
-    lds_barrier();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       *reinterpret_cast<float4*>(o_dst + cb * 32 + 8 * a + 4 * half) =
           make_float4(acc[cb][4 * a] * inv, acc[cb][4 * a + 1] * inv, acc[cb][4 * a + 2] * inv,
                       acc[cb][4 * a + 3] * inv);
-  if (half == 0) *lse_dst = (l_tot > 0.f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (half == 0) *lse_dst = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace mla
