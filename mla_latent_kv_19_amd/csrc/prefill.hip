@@ -1,10 +1,367 @@
-// Causal prefill (un-absorbed form).  Not built yet: the entry point reports
-// hipErrorNotSupported, which the C ABI maps to MLA_ERR_UNSUPPORTED.
+// Causal MLA prefill in the un-absorbed form.
+//
+// "Teardown: DeepSeek-V3", section 4: per head the keys are [W_UK c; k_R]
+// (128 + 64 values, k_R shared by all heads) and the values W_UV c (128);
+// scores are scaled by 1/sqrt(128 + 64).  "DeepSeek-V3" (llm-vis explorer),
+// "Scaled dot-product attention": causal mask (position i sees keys <= i) and
+// online renormalisation over key blocks.
+//
+// For T queries per sequence the un-absorbed form needs 2.8x fewer FLOPs than
+// attending in the 576-wide latent space, so prefill rebuilds per-head keys and
+// values once and runs a flash-attention kernel over them:
+//
+//   prefill_kv_kernel   K_C[b,h,t,:] = W_UK[h] c_t          (bf16, [B,H,Lpad,128])
+//                       V^T[b,h,:,t] = (c_t W_UV[h])^T      (bf16, [B,H,128,Lpad],
+//                                                             keys permuted in 16s)
+//   prefill_attn_kernel out[b,i,h,:] = softmax(q . k * scale, causal) V
+//
+// Work decomposition (MI355X):
+//   * reconstruction: one work-group per (sequence, head, 128 positions); the
+//     128x512 latent block is the A operand read straight from the paged
+//     cache, W_UK[h] and W_UV[h] are staged through LDS in 64-row slices;
+//   * attention: one work-group of 4 waves per (sequence, head, 128 queries),
+//     wave w owning 32 queries; 64-key tiles ([K_C | k_R] and V^T) stream into
+//     LDS with direct-to-LDS loads, double buffered; S^T = K Q^T and
+//     O^T += V^T P^T run on MFMA 32x32x16 with P^T taken straight from the
+//     score registers; query blocks are dispatched longest (most keys) first.
 #include "mla_common.h"
 
-extern "C" hipError_t mla_launch_prefill(const uint16_t*, const uint16_t*, const uint16_t*,
-                                         const int32_t*, const int32_t*, const uint16_t*,
-                                         const uint16_t*, uint16_t*, void*, int, int, int, float,
-                                         hipStream_t) {
-  return hipErrorNotSupported;
+namespace mla {
+
+constexpr int kPfThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Key order inside V^T rows.  P^T comes out of the score product with lane
+// half hh holding keys {4hh..4hh+3, 8+4hh..8+4hh+3} of each 16-key step; V^T
+// is stored with each 16-key group in that order so the matching A operand is
+// one contiguous 16-byte read.  pos(t) for t in a group: [0-3, 8-11, 4-7, 12-15].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vt_pos(int t) {
+  const int u = t & 15;
+  const int q = u >> 2;                       // which 4-key quarter
+  const int pq = ((q & 1) << 1) | (q >> 1);   // quarters 0,1,2,3 -> slots 0,2,1,3
+  return (t & ~15) | (pq << 2) | (u & 3);
+}
+
+// ===========================================================================
+// Reconstruction
+// ===========================================================================
+constexpr int kWkPitch = 64 + 8;     // bf16 per W_UK LDS row (144 B)
+constexpr int kWvPitch = 128 + 24;   // bf16 per W_UV LDS row (304 B)
+
+__global__ __launch_bounds__(kPfThreads) void prefill_kv_kernel(
+    const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ w_uk,
+    const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_vt,
+    int max_blocks, int n_tblk) {
+  __shared__ __attribute__((aligned(16))) uint16_t wk[128 * kWkPitch];   // [i][j slice]
+  __shared__ __attribute__((aligned(16))) uint16_t wv[64 * kWvPitch];    // [j slice][d]
+
+  const int tblk = blockIdx.x % n_tblk;
+  const int h = (blockIdx.x / n_tblk) % 128;
+  const int b = blockIdx.x / (n_tblk * 128);
+  const int L = seq_lens[b];
+  const int t0 = tblk * 128;
+  if (t0 >= L) return;
+  const int Lpad = max_blocks * 64;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31, wave = tid >> 6;
+  const int q16 = lane & 15, colhalf = (lane >> 4) & 1;
+
+  // A operand rows: token t = t0 + 32*wave + l32 of sequence b.
+  const int t_row = t0 + 32 * wave + l32;
+  const int t_clamped = min(t_row, L - 1);     // rows past L are masked at the store
+  const uint16_t* crow = kv + ((size_t)block_table[(size_t)b * max_blocks + (t_clamped >> 6)] * 64 +
+                               (t_clamped & 63)) * 576 + 8 * half;
+
+  f32x16 acc_k[4], acc_v[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) { acc_k[n] = f32x16{}; acc_v[n] = f32x16{}; }
+
+  const uint16_t* wuk = w_uk + (size_t)h * 128 * 512;
+  const uint16_t* wuv = w_uv + (size_t)h * 512 * 128;
+  const lds_u8* wk_l = to_lds(wk);
+  const lds_u8* wv_l = to_lds(wv);
+  // B operand for K_C (W_UK^T: k = j, n = i): lane reads row i = 32n + l32,
+  // 8 consecutive j at 16*ks + 8*half.
+  const lds_u8* wk_rd = wk_l + (l32 * kWkPitch + 8 * half) * 2;
+  // B operand for V (W_UV: k = j, n = d) by transposed reads: group g = lane/16
+  // supplies rows j = 16*ks + 8*(g/2) + q/4 (+4), columns 32n + 16*(g%2) + 4*(q%4).
+  const lds_u8* wv_rd = wv_l + ((8 * half + (q16 >> 2)) * kWvPitch + 16 * colhalf + 4 * (q16 & 3)) * 2;
+
+  for (int jc = 0; jc < 8; ++jc) {
+    __syncthreads();
+    // W_UK[h][0:128][64jc : +64] -> wk: 128 rows x 8 chunks.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ch = k * kPfThreads + tid;
+      const int i = ch >> 3, c = ch & 7;
+      *reinterpret_cast<uint4*>(&wk[i * kWkPitch + c * 8]) =
+          *reinterpret_cast<const uint4*>(wuk + (size_t)i * 512 + 64 * jc + c * 8);
+    }
+    // W_UV[h][64jc : +64][0:128] -> wv: 64 rows x 16 chunks.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ch = k * kPfThreads + tid;
+      const int j = ch >> 4, c = ch & 15;
+      *reinterpret_cast<uint4*>(&wv[j * kWvPitch + c * 8]) =
+          *reinterpret_cast<const uint4*>(wuv + (size_t)(64 * jc + j) * 128 + c * 8);
+    }
+    bf16x8 a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = ld_global_bf16x8(crow + 64 * jc + 16 * ks);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bf16x8 bk = ld_lds_bf16x8(wk_rd + (32 * n * kWkPitch + 16 * ks) * 2);
+        acc_k[n] = mfma32(a[ks], bk, acc_k[n]);
+        const bf16x4 lo = ld_lds_tr(wv_rd + ((16 * ks) * kWvPitch + 32 * n) * 2);
+        const bf16x4 hi = ld_lds_tr(wv_rd + ((16 * ks + 4) * kWvPitch + 32 * n) * 2);
+        acc_v[n] = mfma32(a[ks], cat(lo, hi), acc_v[n]);
+      }
+    }
+  }
+
+  // acc[n][r]: token t0 + 32*wave + 8*(r/4) + 4*half + r%4, column 32n + l32.
+  uint16_t* kdst = ws_k + ((size_t)(b * 128 + h) * Lpad) * 128;
+  uint16_t* vdst = ws_vt + ((size_t)(b * 128 + h) * 128) * Lpad;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int tb = t0 + 32 * wave + 8 * g + 4 * half;   // first of 4 consecutive tokens
+    if (tb >= Lpad) continue;                           // the last 128-block may overhang
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = 32 * n + l32;
+      bf16x4 vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tb + e;
+        const bool ok = t < L;
+        const __bf16 kvl = (__bf16)(ok ? acc_k[n][4 * g + e] : 0.f);
+        kdst[(size_t)t * 128 + col] = __builtin_bit_cast(uint16_t, kvl);
+        vv[e] = (__bf16)(ok ? acc_v[n][4 * g + e] : 0.f);
+      }
+      // Four consecutive tokens stay contiguous under vt_pos().
+      *reinterpret_cast<bf16x4*>(vdst + (size_t)col * Lpad + vt_pos(tb)) = vv;
+    }
+  }
+}
+
+// ===========================================================================
+// Attention
+// ===========================================================================
+constexpr int kKeyTile = 64;
+constexpr int kKRowChunks = 24;                         // 192 bf16 = 24 x 16 B
+constexpr int kKTileBytes = kKeyTile * kKRowChunks * 16;  // 24576
+constexpr int kVRowChunks = kKeyTile * 2 / 16;          // 8 chunks of 8 keys
+constexpr int kVTileBytes = 128 * kVRowChunks * 16;     // 16384
+constexpr int kStageBytes = kKTileBytes + kVTileBytes;  // 40960
+constexpr int kPfLdsBytes = 2 * kStageBytes;            // 81920
+constexpr int kKSlotsPerThread = kKeyTile * kKRowChunks / kPfThreads;   // 6
+constexpr int kVSlotsPerThread = 128 * kVRowChunks / kPfThreads;        // 4
+
+// Chunk placement (same scheme as the decode page): XOR of the low 3 bits of
+// the chunk index, so 16 consecutive rows reading one chunk hit 16 distinct
+// 4-bank groups of the 64-bank LDS.
+__device__ __forceinline__ int k_swz(int key) {
+  return (((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1) | ((key >> 3) & 1);
+}
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+
+__device__ __forceinline__ void issue_kv_tile(const uint16_t* kc_src,   // ws_k row of key k0
+                                              const uint16_t* kr_page,  // cache block of keys k0..
+                                              const uint16_t* vt_src,   // ws_vt + k0 (row d = 0)
+                                              int Lpad, lds_u8* stage, int tid) {
+  lds_u8* kdst = stage + (tid & ~63) * 16;
+#pragma unroll
+  for (int it = 0; it < kKSlotsPerThread; ++it) {
+    const int slot = it * kPfThreads + tid;
+    const int key = slot / kKRowChunks;
+    const int p = slot - key * kKRowChunks;
+    const int c = p ^ k_swz(key);
+    const void* src = (c < 16) ? static_cast<const void*>(kc_src + (size_t)key * 128 + c * 8)
+                               : static_cast<const void*>(kr_page + (size_t)key * 576 + 512 + (c - 16) * 8);
+    g2lds16(src, kdst + it * kPfThreads * 16);
+  }
+  lds_u8* vdst = stage + kKTileBytes + (tid & ~63) * 16;
+#pragma unroll
+  for (int it = 0; it < kVSlotsPerThread; ++it) {
+    const int slot = it * kPfThreads + tid;
+    const int d = slot >> 3;
+    const int c = (slot & 7) ^ v_swz(d);
+    g2lds16(vt_src + (size_t)d * Lpad + c * 8, vdst + it * kPfThreads * 16);
+  }
+}
+
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_attn_kernel(
+    const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ q_r,
+    const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ ws_k,
+    const uint16_t* __restrict__ ws_vt, uint16_t* __restrict__ out, int B, int T, int max_blocks,
+    int n_qblk, float scale_log2) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char pf_smem[];
+  lds_u8* smem = to_lds(pf_smem);
+
+  // Longest query blocks first: consecutive ids walk (sequence, head) for the
+  // last query block, then the one before, ...
+  const int per_q = B * 128;
+  const int qblk = n_qblk - 1 - (int)(blockIdx.x / per_q);
+  const int bh = blockIdx.x % per_q;
+  const int b = bh / 128, h = bh % 128;
+  const int L = seq_lens[b];
+  const int Lpad = max_blocks * 64;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, half = lane >> 5, l32 = lane & 31, wave = tid >> 6;
+
+  // This lane's query: index i (0..T-1), position L - T + i.
+  const int qi = qblk * 128 + 32 * wave + l32;
+  const bool q_ok = qi < T;
+  const int qpos = L - T + qi;
+  // Keys needed by the work-group: up to the position of its last valid query.
+  const int last_q = min(T - 1, qblk * 128 + 127);
+  const int n_keys = L - T + last_q + 1;
+  const int n_tiles = (n_keys + kKeyTile - 1) / kKeyTile;
+
+  // Q^T as B operands: k-step ks covers dims 16ks .. of [q_C (128); q_R (64)].
+  bf16x8 qreg[12];
+  {
+    const size_t row = ((size_t)b * T + (q_ok ? qi : 0)) * 128 + h;
+    const uint16_t* qc = q_c + row * 128 + 8 * half;
+    const uint16_t* qr = q_r + row * 64 + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qreg[ks] = q_ok ? ld_global_bf16x8(qc + 16 * ks) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qreg[8 + ks] = q_ok ? ld_global_bf16x8(qr + 16 * ks) : bf16x8{};
+  }
+
+  const uint16_t* kc_base = ws_k + ((size_t)(b * 128 + h) * Lpad) * 128;
+  const uint16_t* vt_base = ws_vt + ((size_t)(b * 128 + h) * 128) * Lpad;
+  const int32_t* table = block_table + (size_t)b * max_blocks;
+
+  auto issue = [&](int tile, lds_u8* stage) {
+    const int k0 = tile * kKeyTile;
+    issue_kv_tile(kc_base + (size_t)k0 * 128, kv + (size_t)table[k0 >> 6] * 64 * 576, vt_base + k0,
+                  Lpad, stage, tid);
+  };
+  issue(0, smem);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+
+  // Per-lane LDS read offsets.
+  const int kq_swz = k_swz(l32);                 // key row l32 (+32 for the second tile)
+  const int vt_row = l32;                        // V^T row d = 32n + l32
+  const int vq_swz = v_swz(vt_row);
+
+  for (int i = 0; i < n_tiles; ++i) {
+    lds_u8* cur = smem + (i & 1) * kStageBytes;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (i + 1 < n_tiles) issue(i + 1, smem + ((i + 1) & 1) * kStageBytes);
+
+    const int k0 = i * kKeyTile;
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16{};
+      const lds_u8* krow = cur + (kt * 32 + l32) * kKRowChunks * 16;
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) {
+        const int c = 2 * ks + half;
+        const int p = (c & ~7) | ((c & 7) ^ kq_swz);
+        s[kt] = mfma32(ld_lds_bf16x8(krow + p * 16), qreg[ks], s[kt]);
+      }
+    }
+    // s[kt][r]: key k0 + 32kt + 8*(r/4) + 4*half + r%4, query qi.
+    float x[32];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = q_ok && key <= qpos && key < L;
+        x[16 * kt + r] = vis ? s[kt][r] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[16 * kt + r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m_ref + 8.f;
+    if (move) {
+      const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[n] *= alpha;
+      m_ref = mx;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const float p = fast_exp2(x[r] - m_use);
+      l_run += p;
+      pb[r >> 3][r & 7] = (__bf16)p;
+    }
+    // O^T[128 d x 32 q] += V^T[128 x 16 keys] . P^T over four 16-key steps.
+    const lds_u8* vt = cur + kKTileBytes + vt_row * kVRowChunks * 16;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      const int c = 2 * kstep + half;            // 8 keys of this lane's half
+      const int p = c ^ vq_swz;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bf16x8 av = ld_lds_bf16x8(vt + (32 * n * kVRowChunks + p) * 16);
+        acc[n] = mfma32(av, pb[kstep], acc[n]);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (q_ok) {
+    uint16_t* dst = out + (((size_t)b * T + qi) * 128 + h) * 128;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[n][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * n + 8 * g + 4 * half) = v;
+      }
+  }
+}
+
+}  // namespace mla
+
+extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* out,
+                                         void* workspace, int B, int T, int max_blocks,
+                                         float softmax_scale, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&mla::prefill_attn_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, mla::kPfLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const size_t Lpad = (size_t)max_blocks * 64;
+  uint16_t* ws_k = static_cast<uint16_t*>(workspace);
+  uint16_t* ws_vt = ws_k + (size_t)B * 128 * Lpad * 128;
+  int n_tblk = (int)((Lpad + 127) / 128);
+  {
+    void* args[] = {&kv, &block_table, &seq_lens, &w_uk, &w_uv, &ws_k, &ws_vt, &max_blocks, &n_tblk};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mla::prefill_kv_kernel),
+                                         dim3(B * 128 * n_tblk), dim3(mla::kPfThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  int n_qblk = (T + 127) / 128;
+  float scale_log2 = softmax_scale * mla::kLog2e;
+  void* args[] = {&q_c, &q_r, &kv, &block_table, &seq_lens, &ws_k, &ws_vt, &out,
+                  &B, &T, &max_blocks, &n_qblk, &scale_log2};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mla::prefill_attn_kernel),
+                         dim3(B * 128 * n_qblk), dim3(mla::kPfThreads), args, mla::kPfLdsBytes, stream);
 }
