@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-collection mode: K decode steps plus a 1 GiB device copy "
+                         "(the byte-count calibration for HBM counters), nothing else")
     return ap.parse_args()
 
 
@@ -105,6 +108,46 @@ def cpu_baseline(wl, inp_meta, budget_s):
                       f"{tokens} KV tokens), un-absorbed fp64 numpy oracle, {spent:.1f} s"}
 
 
+def bench_prefill(steps, warmup):
+    """Causal prefill, T = L = 4096, B = 1 (reconstruction + attention), on MFMA."""
+    import torch
+    from mla_latent_kv_19_amd import api, synth
+    wl = synth.WORKLOADS["prefill"]
+    inp = synth.make_inputs(wl)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q_c, q_r, kv = dev(inp.q_c), dev(inp.q_r), dev(inp.kv_cache)
+    table = torch.from_numpy(inp.block_table).cuda()
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    w_uk, w_uv = dev(inp.w_uk), dev(inp.w_uv)
+    T = wl.tq
+    out = torch.empty((1, T, 128, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(api.prefill_workspace_bytes(1, table.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        api.prefill(q_c, q_r, kv, table, lens, w_uk, w_uv, wl.scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = T * (T + 1) // 2
+    flops = pairs * 128 * 2 * (192 + 128) + T * 128 * 512 * 256 * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"{wl.name}: {wl.note}", "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+            "tflops": tflops, "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flop": flops}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -146,6 +189,18 @@ def main():
         api.absorb_q(q_c, w_uk, out=q_lat)
         api.decode_paged(q_lat, q_r, kv, table, lens, wl.scale, splits, part_o, part_lse)
         api.combine(part_o, part_lse, w_uv, out=out)
+
+    if args.profile:
+        for _ in range(args.warmup + args.steps):
+            step()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": True, "steps": args.warmup + args.steps,
+                          "kv_bytes_per_decode": kv_tokens * ROW_BYTES, "copy_bytes": 1 << 30}))
+        return
 
     for _ in range(args.warmup):
         step()
@@ -220,6 +275,7 @@ def main():
         "wall_s": wall,
         "input_gen_s": gen_s,
     }
+    res["prefill"] = bench_prefill(max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, meta, args.cpu_seconds)
     else:
