@@ -34,6 +34,14 @@ def hipcc():
     return path
 
 
+# Per-file extra flags.  decode.hip keeps all 256 AGPRs for its output
+# accumulators (written by inline-asm MFMAs) and needs the compiler's own MFMAs
+# (the score product) to accumulate in VGPRs.
+EXTRA_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def build(verbose=False):
     """Compile all sources and link libmla.so; returns the library path."""
     objdir = os.path.join(PKG, "_build")
@@ -44,7 +52,8 @@ def build(verbose=False):
     for src in sources:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc(), *HIPCC_FLAGS, *lang, "-c", src, "-o", obj]
+        extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+        cmd = [hipcc(), *HIPCC_FLAGS, *extra, *lang, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd))
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

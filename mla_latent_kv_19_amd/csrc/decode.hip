@@ -7,65 +7,82 @@
 //   s_t   = (q_lat[b,i,h] . c_t + q_R[b,i,h] . k_R,t) * scale
 //   o_s   = sum_t softmax(s)_t c_t            (512 wide, fp32)
 //   lse_s = ln sum_t exp(s_t)
-// with the softmax renormalised online, one 64-token page at a time.
+// with the softmax renormalised online, 32 tokens at a time.
 //
 // Work decomposition (MI355X: 256 CUs, 64-wide waves, 160 KB LDS per CU):
 //   * one work-group of 4 waves per (sequence, split, query); the 128 heads
-//     share each cached row, so a page is loaded once into LDS and used by all
+//     share each cached row, so a tile is loaded once into LDS and used by all
 //     128 heads: wave w owns heads 32w .. 32w+31;
-//   * each wave keeps its 32 queries (576 wide, bf16) in registers as the B
-//     operand and its output O^T (512 x 32 heads, fp32) in 256 accumulator
-//     registers;
-//   * per 32-token slice: S^T[32 tok x 32 heads] = K[32 x 576] . Q^T
-//     (36 MFMA 32x32x16, K read from LDS with 16-byte reads), online softmax in
+//   * each wave keeps its 32 latent queries (512 wide, bf16) in 128 VGPRs as the
+//     B operand (the 64-wide rotary queries of all heads sit in LDS) and its
+//     output O^T (512 x 32 heads, fp32) in the 256 AGPRs;
+//   * per 32-token tile: S^T[32 tok x 32 heads] = K[32 x 576] . Q^T as two
+//     independent MFMA 32x32x16 chains (even / odd k-steps), online softmax in
 //     registers (lane = head), then O^T[512 x 32] += V^T[512 x 32 tok] . P^T
-//     (32 MFMA; V^T read from the same LDS tile with transposed reads, P^T taken
-//     straight from the score registers: no shuffles);
-//   * pages stream global -> LDS with 16-byte direct-to-LDS loads, double
-//     buffered: page n+1 is in flight while page n is multiplied.
+//     (32 MFMA; V^T read from the same LDS tile with transposed reads, P^T is the
+//     score registers reinterpreted: no shuffles);
+//   * software pipeline: the softmax of tile n-1 is issued alongside the score
+//     MFMAs of tile n, then the value MFMAs of tile n-1 follow;
+//   * tiles stream global -> LDS with 16-byte direct-to-LDS loads through a ring
+//     of 4 stages (2 in flight while 2 are being multiplied), one barrier per tile.
 #include "mla_common.h"
 
 namespace mla {
 
 constexpr int kDecThreads = 256;
-constexpr int kTok = 64;                       // tokens per cache block
-constexpr int kRowVals = 576;                  // 512 latent + 64 rotary
-constexpr int kRowBytes = kRowVals * 2;        // 1152
-constexpr int kChunks = kRowBytes / 16;        // 72 sixteen-byte chunks per row
-constexpr int kPageBytes = kTok * kRowBytes;   // 73728
-constexpr int kLoadsPerThread = kPageBytes / 16 / kDecThreads;  // 18
-constexpr int kDecLdsBytes = 2 * kPageBytes;   // double buffer
+constexpr int kTok = 64;                        // tokens per cache block
+constexpr int kRowVals = 576;                   // 512 latent + 64 rotary
+constexpr int kRowBytes = kRowVals * 2;         // 1152
+constexpr int kChunks = kRowBytes / 16;         // 72 sixteen-byte chunks per row
+constexpr int kTileTok = 32;                    // tokens per pipeline stage
+constexpr int kTileBytes = kTileTok * kRowBytes;                 // 36864
+constexpr int kRing = 4;                        // stages in the LDS ring
+constexpr int kLoadsPerThread = kTileBytes / 16 / kDecThreads;  // 9
+constexpr int kQrBytes = 128 * 64 * 2;          // rotary queries of the 128 heads
+constexpr int kDecLdsBytes = kRing * kTileBytes + kQrBytes;      // 163840
 
-static_assert(kLoadsPerThread * 16 * kDecThreads == kPageBytes, "page must split evenly");
+static_assert(kLoadsPerThread * 16 * kDecThreads == kTileBytes, "tile must split evenly");
+static_assert(kDecLdsBytes <= 160 * 1024, "LDS budget");
 
 // Lazy renormalisation threshold (log2 units): unnormalised weights stay <= 2^8.
 constexpr float kLazy = 8.f;
 
-// LDS placement of chunk c of token row t: the low three bits of the chunk
-// index are XORed with a per-row pattern so that both the 16-byte row reads of
-// the score product (8 rows, same chunk) and the transposed reads of the value
-// product (4 rows x 2 adjacent chunks) hit distinct banks.
-__device__ __forceinline__ int row_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-__device__ __forceinline__ int chunk_off(int t, int c) {
-  return (t * kChunks + (c ^ row_swz(t))) * 16;
+// LDS layout of a 32-row tile.  The tile is cut into 4 x 9 blocks of 8 rows x
+// 8 sixteen-byte chunks (1 KB each, block (t/8, c/8) at (t/8)*9 + c/8); inside a
+// block, row t%8 holds its 8 chunks with the chunk index XORed by bits 1..3 of
+// the row.  On the 64-bank LDS both access patterns are conflict-free: 16
+// consecutive rows reading one chunk (score operand, 16 lanes per cycle) and 4
+// consecutive rows x 4 adjacent chunks (transposed value reads, 32 lanes per
+// cycle).  Because one 64-lane direct-to-LDS load fills exactly one block, each
+// lane's source offset depends only on its lane id and the parity of the row
+// group: the per-tile address work is two scalar adds per load.
+__device__ __forceinline__ int row_swz(int t) {
+  return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1);
+}
+constexpr int kBlkBytes = 1024;                 // 8 rows x 8 chunks
+constexpr int kRowGrpBytes = 9 * kBlkBytes;     // 8 rows x 72 chunks
+
+// Byte offset of (row t, chunk c) inside a tile.
+__device__ __forceinline__ int tile_off(int t, int c) {
+  return (t >> 3) * kRowGrpBytes + (c >> 3) * kBlkBytes + (t & 7) * 128 + ((c & 7) ^ row_swz(t)) * 16;
 }
 
-// All 256 threads: copy one 64-token page into an LDS buffer.  Thread tid
-// fills LDS slots it*256 + tid; each slot's source chunk is chosen so that the
-// slot order realises chunk_off().
-__device__ __forceinline__ void issue_page(const uint16_t* page, lds_u8* buf, int tid) {
-  // Recompute the slot addresses per page instead of keeping 18 of them live
-  // across the loop (the register file is nearly full).
-  asm volatile("" : "+v"(tid));
-  const char* g = reinterpret_cast<const char*>(page);
-  lds_u8* wave_base = buf + (tid & ~63) * 16;
+// All 256 threads: copy 32 consecutive cache rows into an LDS stage.  Wave w
+// fills blocks 4*it + w; lane j of a block loads row 8*(block/9) + j/8, chunk
+// 8*(block%9) + ((j%8) ^ swizzle).  src_lane[0/1] are the lane's offsets for
+// even / odd row groups.
+__device__ __forceinline__ void issue_tile(const uint16_t* rows, lds_u8* stage, int wave,
+                                           const int (&src_lane)[2]) {
+  const char* g = reinterpret_cast<const char*>(rows);
+  // Opaque copies: keeps the compiler from precomputing (and spilling) nine
+  // 64-bit addresses across the tile loop; each load costs one 64-bit add.
+  int o0 = src_lane[0], o1 = src_lane[1];
+  asm volatile("" : "+v"(o0), "+v"(o1));
 #pragma unroll
   for (int it = 0; it < kLoadsPerThread; ++it) {
-    const int slot = it * kDecThreads + tid;
-    const int t = slot / kChunks;
-    const int p = slot - t * kChunks;
-    const int c = p ^ row_swz(t);
-    g2lds16(g + t * kRowBytes + c * 16, wave_base + it * kDecThreads * 16);
+    const int blk = it * 4 + wave;                 // wave-uniform
+    const int rg = blk / 9, cb = blk - rg * 9;
+    g2lds16(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
   }
 }
 
@@ -76,6 +93,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     int num_splits, int num_units, float* __restrict__ part_o, float* __restrict__ part_lse) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dec_smem[];
   lds_u8* smem = to_lds(dec_smem);
+  lds_u8* qr_lds = smem + kRing * kTileBytes;
 
   // Work-group -> (unit = (sequence, split), query).  Consecutive ids go to
   // different XCDs; the Tq work-groups of one unit get ids 8 apart so they
@@ -92,22 +110,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = wave * 32 + l32;
+  int src_lane[2];
+  {
+    const int f = (((lane >> 4) & 1) << 2) | (((lane >> 5) & 1) << 1);
+    src_lane[0] = (lane >> 3) * kRowBytes + ((lane & 7) ^ f) * 16;
+    src_lane[1] = (lane >> 3) * kRowBytes + ((lane & 7) ^ (f | 1)) * 16;
+  }
 
   const int L = seq_lens[b];
   const int n_pages = (L + kTok - 1) / kTok;
   const int per = (n_pages + num_splits - 1) / num_splits;
   const int p0 = min(n_pages, split * per);
   const int n_vis = L - Tq + qi + 1;                  // keys this query sees
-  const int p1 = min(min(n_pages, p0 + per), (n_vis + kTok - 1) / kTok);
-  const int count = p1 - p0;
+  const int T0 = p0 * kTok;                           // first token of the split
+  const int T1 = min(min(n_pages, p0 + per) * kTok, n_vis);
+  const int ntiles = (T1 > T0) ? (T1 - T0 + kTileTok - 1) / kTileTok : 0;
 
-  const size_t row = (size_t)(b * Tq + qi) * 128 + head;   // query row index (H = 128)
+  const size_t qrow = (size_t)(b * Tq + qi) * 128;          // first row of this query's heads
+  const size_t row = qrow + head;
   float* o_dst = part_o + ((size_t)split * B * Tq * 128 + row) * 512;
   float* lse_dst = part_lse + (size_t)split * B * Tq * 128 + row;
 
-  if (count <= 0) {
+  if (ntiles == 0) {
     // Nothing visible in this split: o = 0, lse = -inf.
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
@@ -119,126 +145,237 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   }
 
   const int32_t* table = block_table + (size_t)b * max_blocks;
-  issue_page(kv + (size_t)table[p0] * (kTok * kRowVals), smem, tid);
+  auto tile_rows = [&](int n) {
+    const int t = T0 + n * kTileTok;                  // a tile never crosses a cache block
+    return kv + ((size_t)table[t >> 6] * kTok + (t & (kTok - 1))) * kRowVals;
+  };
+  issue_tile(tile_rows(0), smem, wave, src_lane);
+  if (ntiles > 1) issue_tile(tile_rows(1), smem + kTileBytes, wave, src_lane);
 
-  // Queries as B operands: k-step kk covers dims 16kk .. 16kk+15 of [q_lat; q_R].
-  bf16x8 qreg[36];
+  // Rotary queries of all 128 heads -> LDS, [head][64] with the 8 chunks of a
+  // row XOR-swizzled by bits 1..3 of the head (16 consecutive heads reading one
+  // chunk then hit distinct banks).
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int id = k * kDecThreads + tid;
+    const int h = id >> 3, c = id & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(q_r + (qrow + h) * 64 + c * 8);
+    st_lds16(qr_lds + (h * 8 + (c ^ ((h >> 1) & 7))) * 16, v);
+  }
+
+  // Latent queries as B operands: k-step kk covers dims 16kk .. 16kk+15.
+  bf16x8 qreg[32];
   {
     const uint16_t* ql = q_lat + row * 512 + 8 * half;
-    const uint16_t* qr = q_r + row * 64 + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) qreg[kk] = ld_global_bf16x8(ql + 16 * kk);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qreg[32 + kk] = ld_global_bf16x8(qr + 16 * kk);
   }
 
   f32x16 acc[16];
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) acc[cb] = f32x16{};
-  float m_ref = -INFINITY;   // exponent reference (<= running max + 0), log2 units
+  agpr_settle16(acc);
+  float m_ref = -INFINITY;   // exponent reference, log2 units
   float l_run = 0.f;         // this lane's share of sum 2^(x - m_ref)
 
   // Per-lane LDS offsets.
-  // Score product: lane reads token (l32) of the slice, chunk 2kk + half.
+  // Score operand: lane reads tile row l32, chunk 2kk + half.
   const int sq = row_swz(l32);
-  const int qk_base = l32 * kRowBytes;
+  const int qk_base = (l32 >> 3) * kRowGrpBytes + (l32 & 7) * 128;
+  const lds_u8* qr_rd = qr_lds + head * 128;
+  const int qr_s = (head >> 1) & 7;
   // Transposed value reads: group g = lane/16 (g/2 = half, g%2 = column half),
-  // q = lane%16 supplies row 4*half + q/4 (+8 for the second read), columns
-  // 16*(g%2) + 4*(q%4) .. +3 of the 32-column block.
+  // q = lane%16 supplies tile row 16kt + 8rd + 4*half + q/4, columns
+  // 32cb + 16*(g%2) + 4*(q%4) .. +3.
   const int q16 = lane & 15;
   const int colhalf = (lane >> 4) & 1;
-  const int tr_row = 4 * half + (q16 >> 2);
-  const int st = row_swz(tr_row);
-  const int tr_base = tr_row * kRowBytes + (q16 & 1) * 8;
-  const int tr_c0 = (2 * colhalf + ((q16 & 3) >> 1)) ^ st;        // even column blocks
-  const int tr_c1 = (4 + 2 * colhalf + ((q16 & 3) >> 1)) ^ st;    // odd column blocks
+  const int tr_row = 4 * half + (q16 >> 2);                     // row within its 8-row group
+  const int tr_base = tr_row * 128 + (q16 & 1) * 8;
+  const int tr_cc = 2 * colhalf + ((q16 & 3) >> 1);             // chunk within 4 of the block
+  const int st0 = row_swz(tr_row), st1 = row_swz(tr_row + 8);
+  const int tr_e0 = (tr_cc ^ st0) * 16, tr_o0 = ((4 + tr_cc) ^ st0) * 16;   // even / odd cb, rd = 0
+  const int tr_e1 = (tr_cc ^ st1) * 16, tr_o1 = ((4 + tr_cc) ^ st1) * 16;   // rd = 1
 
-  for (int i = 0; i < count; ++i) {
-    lds_u8* cur = smem + (i & 1) * kPageBytes;
-    // One barrier per page: after it, page i has landed for every wave and
-    // every wave has finished page i-1, whose buffer then takes page i+1.
-    wait_vmcnt<0>();
+  // ---- pipeline stages -----------------------------------------------------
+  auto top = [&](int n) {
+    // Tile n has landed for every wave, every wave is done with tile n-2, whose
+    // stage then takes tile n+2.
+    if (n + 1 < ntiles) wait_vmcnt<kLoadsPerThread>(); else wait_vmcnt<0>();
     lds_barrier();
-    if (i + 1 < count)
-      issue_page(kv + (size_t)table[p0 + i + 1] * (kTok * kRowVals),
-                 smem + ((i + 1) & 1) * kPageBytes, tid);
-
-    const int pg = p0 + i;
-    const int valid = L - pg * kTok;                // rows of this page inside the sequence
-    if (valid < kTok) {
+    if (n + 2 < ntiles) issue_tile(tile_rows(n + 2), smem + ((n + 2) % kRing) * kTileBytes, wave, src_lane);
+    const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
+    if (valid < kTileTok) {
       // Rows past the sequence end may hold anything (NaN): zero them so that
-      // 0-weight tokens contribute exactly 0 to the value product.
-      for (int off = valid * kRowBytes + tid * 16; off < kPageBytes; off += kDecThreads * 16)
-        st_lds_zero16(cur + off);
-      lds_barrier();
+      // 0-weight tokens contribute exactly 0 to the value product.  They are
+      // read by the value product one barrier later.
+      lds_u8* stage = smem + (n % kRing) * kTileBytes;
+      for (int idx = tid; idx < (kTileTok - valid) * kChunks; idx += kDecThreads) {
+        const int t = valid + idx / kChunks;
+        st_lds_zero16(stage + tile_off(t, idx % kChunks));
+      }
     }
+  };
 
+  // Score operand (tile row l32, chunk 2kk + half) and rotary query (k-step 32 + j).
+  auto ld_k = [&](const lds_u8* rd, int kk) {
+    return ld_lds_bf16x8(rd + (kk >> 2) * kBlkBytes + ((2 * (kk & 3) + half) ^ sq) * 16);
+  };
+  auto ld_qr = [&](int j) { return ld_lds_bf16x8(qr_rd + ((2 * j + half) ^ qr_s) * 16); };
+  // Value operand m = 16kt + cb: V^T rows 32cb.., tokens 16kt + {4h..4h+3, 8+4h..}.
+  auto ld_v = [&](const lds_u8* stage, int m) {
+    const int kt = m >> 4, cb = m & 15;
+    const lds_u8* vrow = stage + 2 * kt * kRowGrpBytes + tr_base + (cb >> 1) * kBlkBytes;
+    const bf16x4 lo = ld_lds_tr(vrow + ((cb & 1) ? tr_o0 : tr_e0));
+    const bf16x4 hi = ld_lds_tr(vrow + kRowGrpBytes + ((cb & 1) ? tr_o1 : tr_e1));
+    return cat(lo, hi);
+  };
+
+  // Exponent bookkeeping of one tile from its row maximum (raw score units).
+  auto decide = [&](float mx_raw, float& alpha, bool& resc, float& m_use) {
+    const float mx = mx_raw * scale_log2;                     // log2 units
+    const bool move = mx > m_ref + kLazy;
+    resc = move && m_ref != -INFINITY;          // accumulators are still zero otherwise
+    alpha = resc ? fast_exp2(m_ref - mx) : 1.f;
+    if (move) m_ref = mx;
+    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  };
+  auto half_max = [](float v) {               // max over lanes l and l^32
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                    __builtin_bit_cast(unsigned, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  };
+
+  // The score product of tile n (two independent chains, even / odd k-steps),
+  // with the softmax of tile n-1 (scores se/so) cut into small pieces issued
+  // between the MFMAs.  sched_barrier fences pin the order: the LDS reads stay
+  // 4 k-steps ahead of their MFMA and each VALU piece sits between two MFMAs.
+  // The MFMAs are compiler builtins (VGPR form), so the compiler still inserts
+  // every wait state their results need.  Operands rotate through 6 registers:
+  // the load issued after MFMA kk refills the one MFMA kk-2 used.
+  auto scores_softmax = [&](int n, bool with_sm, const f32x16& sp, f32x16& sn, bf16x8 (&pb)[2],
+                            float& alpha, bool& resc) {
+    const lds_u8* rd = smem + (n % kRing) * kTileBytes + qk_base;
+    const int lim = n_vis - (T0 + (n - 1) * kTileTok + 4 * half);   // tile n-1 rows visible
+    bf16x8 kb[6], qrb[4];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const lds_u8* slice = cur + tb * 32 * kRowBytes;
-      // Score product with the accumulator pinned to VGPRs (the 256 AGPRs hold
-      // the output accumulators); see mfma32_vgpr.
-      f32x16 s;
+    for (int j = 0; j < 4; ++j) kb[j] = ld_k(rd, j);
+    float x[16];
+    float mx = -INFINITY, m_use = 0.f, sum = 0.f;
+    alpha = 1.f;
+    resc = false;
+    f32x16 ae = {}, ao = {};
 #pragma unroll
-      for (int kk = 0; kk < 36; ++kk) {
-        const int c = 8 * (kk >> 2) + ((2 * (kk & 3) + half) ^ sq);
-        const bf16x8 kop = ld_lds_bf16x8(slice + qk_base + c * 16);
-        if (kk == 0)
-          s = mfma32_vgpr_first(kop, qreg[kk]);
-        else
-          mfma32_vgpr_acc(s, kop, qreg[kk]);
-      }
-      mfma_vgpr_settle(s);
-      // s[r] is token tok0 + 8*(r/4) + r%4 of this slice for head `head`.
-      const int tok0 = pg * kTok + tb * 32 + 4 * half;
-      float x[16];
-      float mx = -INFINITY;
+    for (int kk = 0; kk < 36; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 qop = (kk < 32) ? qreg[kk] : qrb[kk - 32];
+      if (kk & 1)
+        ao = mfma32(kb[kk % 6], qop, ao);
+      else
+        ae = mfma32(kb[kk % 6], qop, ae);
+      if (kk + 4 < 36) kb[(kk + 4) % 6] = ld_k(rd, kk + 4);
+      if (kk >= 28 && kk < 32) qrb[kk - 28] = ld_qr(kk - 28);
+      if (!with_sm) continue;
+      if (kk < 8) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = tok0 + 8 * (r >> 2) + (r & 3);
-        x[r] = (t < n_vis) ? s[r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy renormalisation: the exponent reference m_ref only moves when the
-      // slice maximum exceeds it by more than kLazy (so p <= 2^kLazy); the
-      // accumulators are rescaled only then, and not at all on the first
-      // visible slice, when they are still zero.
-      const bool move = mx > m_ref + kLazy;
-      if (__any(move && m_ref != -INFINITY)) {
-        const float alpha = move ? fast_exp2(m_ref - mx) : 1.f;
-        l_run *= alpha;
-        agpr_scale_begin();
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) MLA_AGPR_SCALE(acc[cb][r], alpha);
-        agpr_scale_end();
-      }
-      if (move) m_ref = mx;
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(x[r] - m_use);
-        l_run += p;
-        pb[r >> 3][r & 7] = (__bf16)p;
-      }
-      // O^T += V^T . P^T over the slice's two 16-token k-steps.
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const lds_u8* vrow = slice + (16 * kt) * kRowBytes + tr_base;
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb) {
-          const int coff = (8 * (cb >> 1) + ((cb & 1) ? tr_c1 : tr_c0)) * 16;
-          const bf16x4 lo = ld_lds_tr(vrow + coff);
-          const bf16x4 hi = ld_lds_tr(vrow + 8 * kRowBytes + coff);
-          acc[cb] = mfma32(cat(lo, hi), pb[kt], acc[cb]);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * kk + e;
+          x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
+          mx = fmaxf(mx, x[r]);
         }
+      } else if (kk == 8) {
+        decide(half_max(mx), alpha, resc, m_use);
+      } else if (kk < 25) {
+        const int r = kk - 9;
+        x[r] = fast_exp2(fmaf(x[r], scale_log2, -m_use));
+        sum += x[r];
+      } else if (kk < 29) {
+        const int j = kk - 25;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pb[j >> 1][4 * (j & 1) + e] = (__bf16)x[4 * j + e];
+      } else if (kk == 29) {
+        l_run = l_run * alpha + sum;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    sn = ae + ao;
+  };
+
+  // Softmax of tile n alone (last tile): same arithmetic as the pieces above.
+  auto softmax_tail = [&](int n, const f32x16& sp, bf16x8 (&pb)[2], float& alpha, bool& resc) {
+    const int lim = n_vis - (T0 + n * kTileTok + 4 * half);
+    float x[16];
+    float mx = -INFINITY, m_use, sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    decide(half_max(mx), alpha, resc, m_use);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = fast_exp2(fmaf(x[r], scale_log2, -m_use));
+      sum += x[r];
+      pb[r >> 3][r & 7] = (__bf16)x[r];
+    }
+    l_run = l_run * alpha + sum;
+  };
+
+  // Rare rescale, then O^T += V^T . P^T for tile n (32 MFMAs, value operands
+  // read 3 ahead with transposed LDS reads).
+  auto rescale_and_pv = [&](int n, bf16x8 (&pb)[2], float alpha, bool resc) {
+    valu_to_mfma_settle(pb[0], pb[1]);
+    if (__any(resc)) {
+      agpr_settle16(acc);
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) MLA_AGPR_SCALE(acc[cb][r], alpha);
+      agpr_settle16(acc);
+    }
+    const lds_u8* stage = smem + (n % kRing) * kTileBytes;
+    // Operands rotate through 5 registers; the load after MFMA m refills the
+    // one MFMA m-2 used (see the note on the score product).
+    bf16x8 vb[5];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) vb[j] = ld_v(stage, j);
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                   : "+a"(acc[m & 15]) : "v"(vb[m % 5]), "v"(pb[m >> 4]));
+      if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, m + 3);
+    }
+  };
+
+  // ---- prologue: scores of tile 0 ----
+  f32x16 sc;
+  {
+    bf16x8 pb[2];
+    float alpha;
+    bool resc;
+    top(0);
+    scores_softmax(0, false, sc, sc, pb, alpha, resc);
   }
 
+  // ---- steady state: softmax(n-1) + scores(n), then values(n-1) ----
+  for (int n = 1; n < ntiles; ++n) {
+    top(n);
+    bf16x8 pb[2];
+    float alpha;
+    bool resc;
+    f32x16 sn;
+    scores_softmax(n, true, sc, sn, pb, alpha, resc);
+    rescale_and_pv(n - 1, pb, alpha, resc);
+    sc = sn;
+  }
+  {
+    bf16x8 pb[2];
+    float alpha;
+    bool resc;
+    softmax_tail(ntiles - 1, sc, pb, alpha, resc);
+    rescale_and_pv(ntiles - 1, pb, alpha, resc);
+  }
+
+  agpr_settle16(acc);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
 #pragma unroll

@@ -66,6 +66,31 @@ __device__ __forceinline__ void mfma32_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_vgpr_settle(f32x16& d) {
   asm volatile("s_nop 15\n\ts_nop 15" : "+v"(d));
 }
+__device__ __forceinline__ void mfma_vgpr_settle2(f32x16& d0, f32x16& d1) {
+  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(d0), "+v"(d1));
+}
+
+// Value-product MFMA accumulating into AGPRs.  Used when every AGPR holds an
+// output accumulator and the compiler's own MFMAs are kept in VGPR form
+// (-mllvm -amdgpu-mfma-vgpr-form for that translation unit).  The compiler
+// does not see these as MFMAs, so the callers keep these rules:
+//  * the B operand written by VALU is passed through valu_to_mfma_settle()
+//    first (VALU write -> MFMA operand read needs wait states);
+//  * every accumulator goes through agpr_settle16() before anything other
+//    than another of these MFMAs reads it, and after a VALU/accvgpr write of
+//    it before the next MFMA reads it (MFMA write -> read: 32 wait states).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void valu_to_mfma_settle(bf16x8& b0, bf16x8& b1) {
+  asm volatile("s_nop 4" : "+v"(b0), "+v"(b1));
+}
+__device__ __forceinline__ void agpr_settle16(f32x16 (&a)[16]) {
+  asm volatile("s_nop 15\n\ts_nop 15"
+               : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(a[4]), "+a"(a[5]),
+                 "+a"(a[6]), "+a"(a[7]), "+a"(a[8]), "+a"(a[9]), "+a"(a[10]), "+a"(a[11]),
+                 "+a"(a[12]), "+a"(a[13]), "+a"(a[14]), "+a"(a[15]));
+}
 
 // In-place scaling of one accumulator element held in an AGPR (VALU cannot
 // read AGPRs directly).  agpr_scale_begin/end bracket a run of these with the
@@ -91,6 +116,11 @@ __device__ __forceinline__ bf16x8 ld_global_bf16x8(const uint16_t* p) {
 
 __device__ __forceinline__ bf16x8 ld_lds_bf16x8(const lds_u8* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+__device__ __forceinline__ void st_lds16(lds_u8* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
 }
 
 __device__ __forceinline__ void st_lds_zero16(lds_u8* p) {
