@@ -21,10 +21,12 @@
 //     registers (lane = head), then O^T[512 x 32] += V^T[512 x 32 tok] . P^T
 //     (32 MFMA; V^T read from the same LDS tile with transposed reads, P^T is the
 //     score registers reinterpreted: no shuffles);
-//   * software pipeline: the softmax of tile n-1 is issued alongside the score
-//     MFMAs of tile n, then the value MFMAs of tile n-1 follow;
+//   * software pipeline: the score MFMAs of tile n, then the value MFMAs of
+//     tile n-1 with the softmax of tile n issued in pieces between them;
 //   * tiles stream global -> LDS with 16-byte direct-to-LDS loads through a ring
-//     of 4 stages (2 in flight while 2 are being multiplied), one barrier per tile.
+//     of 4 stages (2 in flight while 2 are being multiplied), one barrier per
+//     tile; the loads of a tile are spread over the score MFMAs of the tile two
+//     ahead.
 #include "mla_common.h"
 
 namespace mla {
@@ -47,6 +49,11 @@ static_assert(kDecLdsBytes <= 160 * 1024, "LDS budget");
 // Lazy renormalisation threshold (log2 units): unnormalised weights stay <= 2^8.
 constexpr float kLazy = 8.f;
 
+// The nine loads of the tile two ahead are issued one every fourth score
+// MFMA (after k-steps 1, 5, ..., 33): piece index, or -1.
+__host__ __device__ constexpr int qk_piece(int kk) { return (kk & 3) == 1 ? (kk >> 2) : -1; }
+static_assert(qk_piece(33) == 8 && qk_piece(35) == -1, "nine pieces over 36 k-steps");
+
 // LDS layout of a 32-row tile.  The tile is cut into 4 x 9 blocks of 8 rows x
 // 8 sixteen-byte chunks (1 KB each, block (t/8, c/8) at (t/8)*9 + c/8); inside a
 // block, row t%8 holds its 8 chunks with the chunk index XORed by bits 1..3 of
@@ -67,10 +74,23 @@ __device__ __forceinline__ int tile_off(int t, int c) {
   return (t >> 3) * kRowGrpBytes + (c >> 3) * kBlkBytes + (t & 7) * 128 + ((c & 7) ^ row_swz(t)) * 16;
 }
 
-// All 256 threads: copy 32 consecutive cache rows into an LDS stage.  Wave w
-// fills blocks 4*it + w; lane j of a block loads row 8*(block/9) + j/8, chunk
-// 8*(block%9) + ((j%8) ^ swizzle).  src_lane[0/1] are the lane's offsets for
-// even / odd row groups.
+// All 256 threads: copy 32 consecutive cache rows into an LDS stage, one of 9
+// pieces per call.  Wave w fills blocks 4*it + w; lane j of a block loads row
+// 8*(block/9) + j/8, chunk 8*(block%9) + ((j%8) ^ swizzle).  o0 / o1 are the
+// lane's offsets for even / odd row groups.
+__device__ __forceinline__ void issue_piece(const char* g, lds_u8* stage, int wave, int it, int o0,
+                                            int o1) {
+  const int blk = it * 4 + wave;                 // wave-uniform
+  const int rg = blk / 9, cb = blk - rg * 9;
+  g2lds16(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
+}
+__device__ __forceinline__ void issue_piece_opaque(const char* g, lds_u8* stage, int wave, int it,
+                                                   int o0, int o1) {
+  const int blk = it * 4 + wave;                 // wave-uniform
+  const int rg = blk / 9, cb = blk - rg * 9;
+  g2lds16_opaque(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
+}
+
 __device__ __forceinline__ void issue_tile(const uint16_t* rows, lds_u8* stage, int wave,
                                            const int (&src_lane)[2]) {
   const char* g = reinterpret_cast<const char*>(rows);
@@ -79,11 +99,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* rows, lds_u8* stage, 
   int o0 = src_lane[0], o1 = src_lane[1];
   asm volatile("" : "+v"(o0), "+v"(o1));
 #pragma unroll
-  for (int it = 0; it < kLoadsPerThread; ++it) {
-    const int blk = it * 4 + wave;                 // wave-uniform
-    const int rg = blk / 9, cb = blk - rg * 9;
-    g2lds16(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
-  }
+  for (int it = 0; it < kLoadsPerThread; ++it) issue_piece(g, stage, wave, it, o0, o1);
 }
 
 __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
@@ -197,12 +213,27 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   const int tr_e1 = (tr_cc ^ st1) * 16, tr_o1 = ((4 + tr_cc) ^ st1) * 16;   // rd = 1
 
   // ---- pipeline stages -----------------------------------------------------
-  auto top = [&](int n) {
+  // Tile n+2, loaded in pieces between the score MFMAs of tile n: a burst of
+  // nine direct-to-LDS loads per wave would stall the wave at issue while the
+  // address unit drains the other waves' loads.
+  struct Next {
+    const char* g;
+    lds_u8* stage;
+    int o0, o1;
+  };
+  auto top = [&](int n, Next& nx) {
     // Tile n has landed for every wave, every wave is done with tile n-2, whose
     // stage then takes tile n+2.
     if (n + 1 < ntiles) wait_vmcnt<kLoadsPerThread>(); else wait_vmcnt<0>();
     lds_barrier();
-    if (n + 2 < ntiles) issue_tile(tile_rows(n + 2), smem + ((n + 2) % kRing) * kTileBytes, wave, src_lane);
+    nx.g = nullptr;
+    if (n + 2 < ntiles) {
+      nx.g = reinterpret_cast<const char*>(tile_rows(n + 2));
+      nx.stage = smem + ((n + 2) % kRing) * kTileBytes;
+      nx.o0 = src_lane[0];
+      nx.o1 = src_lane[1];
+      asm volatile("" : "+v"(nx.o0), "+v"(nx.o1));
+    }
     const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
     if (valid < kTileTok) {
       // Rows past the sequence end may hold anything (NaN): zero them so that
@@ -245,24 +276,51 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
   };
 
-  // The score product of tile n (two independent chains, even / odd k-steps),
-  // with the softmax of tile n-1 (scores se/so) cut into small pieces issued
-  // between the MFMAs.  sched_barrier fences pin the order: the LDS reads stay
-  // 4 k-steps ahead of their MFMA and each VALU piece sits between two MFMAs.
-  // The MFMAs are compiler builtins (VGPR form), so the compiler still inserts
-  // every wait state their results need.  Operands rotate through 6 registers:
-  // the load issued after MFMA kk refills the one MFMA kk-2 used.
-  auto scores_softmax = [&](int n, bool with_sm, const f32x16& sp, f32x16& sn, bf16x8 (&pb)[2],
-                            float& alpha, bool& resc) {
+  // Online softmax of one tile (scores sp, lane = head, 16 tokens per lane) cut
+  // into 30 small steps, so that it can be issued between the MFMAs of the
+  // value product: steps 0-7 mask and maximum, 8 the exponent reference, 9-24
+  // the exponentials, 25-28 the bf16 packing of P, 29 the running sum.  lim:
+  // rows of the tile this lane's query may see.
+  struct Softmax {
+    float x[16];
+    float mx = -INFINITY, m_use = 0.f, sum = 0.f;
+  };
+  auto sm_step = [&](int k, int lim, Softmax& st, const f32x16& sp, bf16x8 (&pb)[2], float& alpha,
+                     bool& resc) {
+    if (k < 8) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * k + e;
+        st.x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
+        st.mx = fmaxf(st.mx, st.x[r]);
+      }
+    } else if (k == 8) {
+      decide(half_max(st.mx), alpha, resc, st.m_use);
+    } else if (k < 25) {
+      const int r = k - 9;
+      st.x[r] = fast_exp2(fmaf(st.x[r], scale_log2, -st.m_use));
+      st.sum += st.x[r];
+    } else if (k < 29) {
+      const int j = k - 25;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pb[j >> 1][4 * (j & 1) + e] = (__bf16)st.x[4 * j + e];
+    } else if (k == 29) {
+      l_run = l_run * alpha + st.sum;
+    }
+  };
+  auto tile_lim = [&](int n) { return n_vis - (T0 + n * kTileTok + 4 * half); };
+
+  // Score product of tile n, two independent MFMA chains (even / odd k-steps),
+  // with the nine loads of tile n+2 (if any) spread over it.  sched_barrier
+  // fences pin the order: the LDS reads stay 4 k-steps ahead of their MFMA.
+  // The MFMAs are compiler builtins (VGPR form), so the compiler inserts every
+  // wait state their results need.  Operands rotate through 6 registers: the
+  // load issued after MFMA kk refills the one MFMA kk-2 used.
+  auto scores = [&](int n, const Next& nx, f32x16& sn) {
     const lds_u8* rd = smem + (n % kRing) * kTileBytes + qk_base;
-    const int lim = n_vis - (T0 + (n - 1) * kTileTok + 4 * half);   // tile n-1 rows visible
     bf16x8 kb[6], qrb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = ld_k(rd, j);
-    float x[16];
-    float mx = -INFINITY, m_use = 0.f, sum = 0.f;
-    alpha = 1.f;
-    resc = false;
     f32x16 ae = {}, ao = {};
 #pragma unroll
     for (int kk = 0; kk < 36; ++kk) {
@@ -274,55 +332,20 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
         ae = mfma32(kb[kk % 6], qop, ae);
       if (kk + 4 < 36) kb[(kk + 4) % 6] = ld_k(rd, kk + 4);
       if (kk >= 28 && kk < 32) qrb[kk - 28] = ld_qr(kk - 28);
-      if (!with_sm) continue;
-      if (kk < 8) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * kk + e;
-          x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
-          mx = fmaxf(mx, x[r]);
-        }
-      } else if (kk == 8) {
-        decide(half_max(mx), alpha, resc, m_use);
-      } else if (kk < 25) {
-        const int r = kk - 9;
-        x[r] = fast_exp2(fmaf(x[r], scale_log2, -m_use));
-        sum += x[r];
-      } else if (kk < 29) {
-        const int j = kk - 25;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pb[j >> 1][4 * (j & 1) + e] = (__bf16)x[4 * j + e];
-      } else if (kk == 29) {
-        l_run = l_run * alpha + sum;
-      }
+      if (qk_piece(kk) >= 0 && nx.g != nullptr)
+        issue_piece_opaque(nx.g, nx.stage, wave, qk_piece(kk), nx.o0, nx.o1);
     }
     __builtin_amdgcn_sched_barrier(0);
     sn = ae + ao;
   };
 
-  // Softmax of tile n alone (last tile): same arithmetic as the pieces above.
-  auto softmax_tail = [&](int n, const f32x16& sp, bf16x8 (&pb)[2], float& alpha, bool& resc) {
-    const int lim = n_vis - (T0 + n * kTileTok + 4 * half);
-    float x[16];
-    float mx = -INFINITY, m_use, sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
-      mx = fmaxf(mx, x[r]);
-    }
-    decide(half_max(mx), alpha, resc, m_use);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = fast_exp2(fmaf(x[r], scale_log2, -m_use));
-      sum += x[r];
-      pb[r >> 3][r & 7] = (__bf16)x[r];
-    }
-    l_run = l_run * alpha + sum;
-  };
-
   // Rare rescale, then O^T += V^T . P^T for tile n (32 MFMAs, value operands
-  // read 3 ahead with transposed LDS reads).
-  auto rescale_and_pv = [&](int n, bf16x8 (&pb)[2], float alpha, bool resc) {
+  // read 3 ahead with transposed LDS reads and rotating through 5 registers).
+  // With a next tile (scores sp), its softmax runs in pieces between the value
+  // MFMAs and leaves P, alpha and the rescale flag for the next call in
+  // pb2 / alpha2 / resc2.
+  auto rescale_and_pv = [&](int n, bf16x8 (&pb)[2], float alpha, bool resc, bool with_sm,
+                            const f32x16& sp, bf16x8 (&pb2)[2], float& alpha2, bool& resc2) {
     valu_to_mfma_settle(pb[0], pb[1]);
     if (__any(resc)) {
       agpr_settle16(acc);
@@ -333,8 +356,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       agpr_settle16(acc);
     }
     const lds_u8* stage = smem + (n % kRing) * kTileBytes;
-    // Operands rotate through 5 registers; the load after MFMA m refills the
-    // one MFMA m-2 used (see the note on the score product).
+    const int lim = tile_lim(n + 1);
+    Softmax st;
+    alpha2 = 1.f;
+    resc2 = false;
     bf16x8 vb[5];
 #pragma unroll
     for (int j = 0; j < 3; ++j) vb[j] = ld_v(stage, j);
@@ -343,36 +368,43 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                    : "+a"(acc[m & 15]) : "v"(vb[m % 5]), "v"(pb[m >> 4]));
       if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, m + 3);
+      if (with_sm && m < 30) sm_step(m, lim, st, sp, pb2, alpha2, resc2);
     }
   };
 
-  // ---- prologue: scores of tile 0 ----
-  f32x16 sc;
+  // ---- prologue: scores and softmax of tile 0 ----
+  bf16x8 pb[2];
+  float alpha = 1.f;
+  bool resc = false;
   {
-    bf16x8 pb[2];
-    float alpha;
-    bool resc;
-    top(0);
-    scores_softmax(0, false, sc, sc, pb, alpha, resc);
+    f32x16 s0;
+    Next nx;
+    top(0, nx);
+    scores(0, nx, s0);
+    Softmax st;
+#pragma unroll
+    for (int k = 0; k < 30; ++k) sm_step(k, tile_lim(0), st, s0, pb, alpha, resc);
   }
-
-  // ---- steady state: softmax(n-1) + scores(n), then values(n-1) ----
+  // ---- steady state: scores(n), then values(n-1) with softmax(n) ----
   for (int n = 1; n < ntiles; ++n) {
-    top(n);
-    bf16x8 pb[2];
-    float alpha;
-    bool resc;
+    Next nx;
+    top(n, nx);
     f32x16 sn;
-    scores_softmax(n, true, sc, sn, pb, alpha, resc);
-    rescale_and_pv(n - 1, pb, alpha, resc);
-    sc = sn;
+    scores(n, nx, sn);
+    bf16x8 pb2[2];
+    float alpha2;
+    bool resc2;
+    rescale_and_pv(n - 1, pb, alpha, resc, true, sn, pb2, alpha2, resc2);
+    pb[0] = pb2[0];
+    pb[1] = pb2[1];
+    alpha = alpha2;
+    resc = resc2;
   }
   {
-    bf16x8 pb[2];
-    float alpha;
-    bool resc;
-    softmax_tail(ntiles - 1, sc, pb, alpha, resc);
-    rescale_and_pv(ntiles - 1, pb, alpha, resc);
+    bf16x8 pd[2];
+    float ad;
+    bool rd;
+    rescale_and_pv(ntiles - 1, pb, alpha, resc, false, f32x16{}, pd, ad, rd);
   }
 
   agpr_settle16(acc);

@@ -145,6 +145,21 @@ __device__ __forceinline__ void g2lds16(const void* g, lds_u8* lds) {
                                    16, 0, 0);
 }
 
+// The same load written as an instruction the compiler does not see.  The
+// builtin is a FLAT-class instruction that may write LDS, so after it the
+// compiler's wait-count model turns every later LDS wait into lgkmcnt(0),
+// which serialises operand reads issued ahead.  The hardware counts this load
+// in vmcnt only; callers wait for it with wait_vmcnt.  It writes no register,
+// and M0 is declared clobbered.  `lds` must be wave-uniform.
+__device__ __forceinline__ void g2lds16_opaque(const void* g, lds_u8* lds) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(m0)
+               : "m0");
+}
+
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in [3:0] and
 // [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
 template <int N>
