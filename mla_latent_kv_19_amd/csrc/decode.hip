@@ -77,15 +77,10 @@ __device__ __forceinline__ int tile_off(int t, int c) {
 // All 256 threads: copy 32 consecutive cache rows into an LDS stage, one of 9
 // pieces per call.  Wave w fills blocks 4*it + w; lane j of a block loads row
 // 8*(block/9) + j/8, chunk 8*(block%9) + ((j%8) ^ swizzle).  o0 / o1 are the
-// lane's offsets for even / odd row groups.
+// lane's offsets for even / odd row groups.  Every direct-to-LDS load of this
+// kernel goes through the opaque form (the kernel sets M0 only there).
 __device__ __forceinline__ void issue_piece(const char* g, lds_u8* stage, int wave, int it, int o0,
                                             int o1) {
-  const int blk = it * 4 + wave;                 // wave-uniform
-  const int rg = blk / 9, cb = blk - rg * 9;
-  g2lds16(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
-}
-__device__ __forceinline__ void issue_piece_opaque(const char* g, lds_u8* stage, int wave, int it,
-                                                   int o0, int o1) {
   const int blk = it * 4 + wave;                 // wave-uniform
   const int rg = blk / 9, cb = blk - rg * 9;
   g2lds16_opaque(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
@@ -261,29 +256,18 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     return cat(lo, hi);
   };
 
-  // Exponent bookkeeping of one tile from its row maximum (raw score units).
-  auto decide = [&](float mx_raw, float& alpha, bool& resc, float& m_use) {
-    const float mx = mx_raw * scale_log2;                     // log2 units
-    const bool move = mx > m_ref + kLazy;
-    resc = move && m_ref != -INFINITY;          // accumulators are still zero otherwise
-    alpha = resc ? fast_exp2(m_ref - mx) : 1.f;
-    if (move) m_ref = mx;
-    m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-  };
-  auto half_max = [](float v) {               // max over lanes l and l^32
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
-                                                    __builtin_bit_cast(unsigned, v), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-  };
-
   // Online softmax of one tile (scores sp, lane = head, 16 tokens per lane) cut
-  // into 30 small steps, so that it can be issued between the MFMAs of the
-  // value product: steps 0-7 mask and maximum, 8 the exponent reference, 9-24
-  // the exponentials, 25-28 the bf16 packing of P, 29 the running sum.  lim:
-  // rows of the tile this lane's query may see.
+  // into 32 small steps, one after each MFMA of the value product.  A wave
+  // issues in order, so a step never waits on a result of the same step: a
+  // transcendental's result is consumed at least one MFMA later.
+  //   0-7    mask rows past the query's limit (lim), running maximum
+  //   8-11   maximum over the lane pair, exponent reference (lazy rescale)
+  //   12-27  the 16 exponentials; the sum lags one step
+  //   28-31  last sum term, bf16 packing of P, running sum l_run
   struct Softmax {
     float x[16];
-    float mx = -INFINITY, m_use = 0.f, sum = 0.f;
+    float mx = -INFINITY, m_use = 0.f, sum = 0.f, mxs = 0.f, arg = 0.f;
+    bool move = false;
   };
   auto sm_step = [&](int k, int lim, Softmax& st, const f32x16& sp, bf16x8 (&pb)[2], float& alpha,
                      bool& resc) {
@@ -295,17 +279,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
         st.mx = fmaxf(st.mx, st.x[r]);
       }
     } else if (k == 8) {
-      decide(half_max(st.mx), alpha, resc, st.m_use);
-    } else if (k < 25) {
-      const int r = k - 9;
+      // maximum over lanes l and l^32 (the two halves of one head's tokens)
+      const unsigned v = __builtin_bit_cast(unsigned, st.mx);
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      st.mx = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    } else if (k == 9) {
+      st.mxs = st.mx * scale_log2;                 // log2 units
+      st.move = st.mxs > m_ref + kLazy;
+    } else if (k == 10) {
+      resc = st.move && m_ref != -INFINITY;       // accumulators are still zero otherwise
+      st.arg = m_ref - st.mxs;
+    } else if (k == 11) {
+      alpha = resc ? fast_exp2(st.arg) : 1.f;
+      if (st.move) m_ref = st.mxs;
+      st.m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    } else if (k < 28) {
+      const int r = k - 12;
       st.x[r] = fast_exp2(fmaf(st.x[r], scale_log2, -st.m_use));
-      st.sum += st.x[r];
-    } else if (k < 29) {
-      const int j = k - 25;
+      if (r > 0) st.sum += st.x[r - 1];
+    } else {
+      const int j = k - 28;
+      if (j == 0) st.sum += st.x[15];
 #pragma unroll
       for (int e = 0; e < 4; ++e) pb[j >> 1][4 * (j & 1) + e] = (__bf16)st.x[4 * j + e];
-    } else if (k == 29) {
-      l_run = l_run * alpha + st.sum;
+      if (j == 3) l_run = l_run * alpha + st.sum;
     }
   };
   auto tile_lim = [&](int n) { return n_vis - (T0 + n * kTileTok + 4 * half); };
@@ -333,7 +330,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       if (kk + 4 < 36) kb[(kk + 4) % 6] = ld_k(rd, kk + 4);
       if (kk >= 28 && kk < 32) qrb[kk - 28] = ld_qr(kk - 28);
       if (qk_piece(kk) >= 0 && nx.g != nullptr)
-        issue_piece_opaque(nx.g, nx.stage, wave, qk_piece(kk), nx.o0, nx.o1);
+        issue_piece(nx.g, nx.stage, wave, qk_piece(kk), nx.o0, nx.o1);
     }
     __builtin_amdgcn_sched_barrier(0);
     sn = ae + ao;
@@ -368,7 +365,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                    : "+a"(acc[m & 15]) : "v"(vb[m % 5]), "v"(pb[m >> 4]));
       if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, m + 3);
-      if (with_sm && m < 30) sm_step(m, lim, st, sp, pb2, alpha2, resc2);
+      if (with_sm) sm_step(m, lim, st, sp, pb2, alpha2, resc2);
     }
   };
 
@@ -383,7 +380,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     scores(0, nx, s0);
     Softmax st;
 #pragma unroll
-    for (int k = 0; k < 30; ++k) sm_step(k, tile_lim(0), st, s0, pb, alpha, resc);
+    for (int k = 0; k < 32; ++k) sm_step(k, tile_lim(0), st, s0, pb, alpha, resc);
   }
   // ---- steady state: scores(n), then values(n-1) with softmax(n) ----
   for (int n = 1; n < ntiles; ++n) {

@@ -149,8 +149,10 @@ __device__ __forceinline__ void g2lds16(const void* g, lds_u8* lds) {
 // builtin is a FLAT-class instruction that may write LDS, so after it the
 // compiler's wait-count model turns every later LDS wait into lgkmcnt(0),
 // which serialises operand reads issued ahead.  The hardware counts this load
-// in vmcnt only; callers wait for it with wait_vmcnt.  It writes no register,
-// and M0 is declared clobbered.  `lds` must be wave-uniform.
+// in vmcnt only; callers wait for it with wait_vmcnt.  It writes no register.
+// M0 is a reserved register the compiler does not track through inline asm:
+// a kernel that uses this form must not also use the builtin (whose M0 set-up
+// the asm could land between).  `lds` must be wave-uniform.
 __device__ __forceinline__ void g2lds16_opaque(const void* g, lds_u8* lds) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds)));
