@@ -6,7 +6,10 @@ A step is one full decode pass over one batch: q-absorption (W_UK folded into
 the query), split-KV attention over the paged latent cache, log-sum-exp
 combine and the W_UV up-projection.  Inputs are seeded synthetic data with
 the shapes of the pages' model (128 heads, latent 512 + rotary 64, content
-head 128) and are resident in HBM before timing starts.
+head 128) and are resident in HBM before timing starts.  Each timed step is
+bracketed by its own HIP events; a 512 MiB write before each step (outside
+the events) leaves no cache state from the previous step.  ms_per_step is the
+mean over the timed steps, with p10 / p50 / p90 alongside.
 
 Prints one JSON line: whole-job throughput in KV-tokens/s, the dominant
 kernel's roofline position (algorithmic bytes / measured launch time against
@@ -32,6 +35,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak
 ROW_BYTES = 576 * 2            # one cached token: latent 512 + rotary key 64, bf16
 FLOP_PER_TOKEN_QUERY = 128 * 2 * (576 + 512)   # scores + value product, all heads
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_headline_traffic.json")
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -204,16 +208,24 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    # Timed steps: HIP events around each step; before each, outside the events,
+    # a 512 MiB write evicts the 4 MB L2s and the 256 MB Infinity Cache, so no
+    # step finds the previous step's weights or queries on chip.
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    for i, (a, b) in enumerate(evs):
+        flush.fill_(i & 255)
+        a.record()
         step()
-    e1.record()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = float(step_ms.mean())
+    del flush
 
     # Per-kernel launch durations, events on the stream the kernels run on.
     def time_kernel(fn, n):
@@ -249,6 +261,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_step_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "flush_between_steps_bytes": FLUSH_BYTES,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

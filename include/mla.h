@@ -41,7 +41,8 @@
  *     Tq (or T) query tokens, which are already in the cache.  Query i of a
  *     sequence sits at position L_b - Tq + i and sees tokens 0 .. L_b - Tq + i.
  *   - Supported shapes: H = 128, d_c = 512, d_r = 64, d_h = d_v = 128,
- *     block_size = 64, 1 <= Tq <= 2 for decode.  Other values return
+ *     block_size = 64, 1 <= Tq <= 8 for decode (one token, or a token and up
+ *     to 7 speculative drafts verified together).  Other values return
  *     MLA_ERR_UNSUPPORTED.  NULL pointers, non-positive sizes, a too-small
  *     workspace or num_splits outside [1, MLA_MAX_SPLITS] return
  *     MLA_ERR_INVALID_ARG.  A HIP launch error returns MLA_ERR_HIP.

@@ -30,7 +30,7 @@ namespace {
 
 // The one shape family the kernels are written for (DeepSeek-V3's MLA dims).
 constexpr int kH = 128, kDC = 512, kDR = 64, kDH = 128, kDV = 128, kBlock = 64;
-constexpr int kMaxTq = 2;
+constexpr int kMaxTq = 8;             // query tokens per sequence in one decode call
 constexpr int kMaxRows = 65536;
 
 int status_of(hipError_t e) {
@@ -49,7 +49,7 @@ const char* mla_strerror(int status) {
   switch (status) {
     case MLA_OK: return "MLA_OK: success";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive size or bad workspace/splits";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape outside H=128, d_c=512, d_r=64, d_h=d_v=128, block 64, Tq<=2";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape outside H=128, d_c=512, d_r=64, d_h=d_v=128, block 64, Tq<=8";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime rejected a kernel launch";
     default: return "unknown mla status";
   }

@@ -83,7 +83,7 @@ def test_decode_argument_errors():
     assert _decode(lib, scale=float("nan")) == E
     assert _decode(lib, H=64) == U
     assert _decode(lib, block_size=16) == U
-    assert _decode(lib, Tq=3) == U
+    assert _decode(lib, Tq=9) == U
     assert _decode(lib, d_r=32) == U
 
 

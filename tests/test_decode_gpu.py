@@ -46,9 +46,39 @@ def test_small_ragged_paged(tq):
     _check_decode(make(wl), what=f"small ragged tq={tq}")
 
 
+@pytest.mark.parametrize("tq", [3, 5, 8])
+def test_speculative_verify_widths(tq):
+    """Tq = 3..8 causal query tokens per sequence (a token plus drafts verified
+    together): every query row against the oracle, ragged lengths, pages
+    crossing split boundaries."""
+    print(f"[case] verify width tq={tq}", flush=True)
+    wl = synth.small_workload(batch=5, tq=tq, len_lo=tq, len_hi=600, seed=131 + tq)
+    _check_decode(make(wl), what=f"verify width tq={tq}")
+
+
+def test_verify_rows_match_single_query():
+    """Query i of a Tq = 5 call equals a Tq = 1 call whose sequence ends at that
+    query's position (GPU vs GPU, same cache and pages)."""
+    print("[case] verify rows vs single-query decode", flush=True)
+    tq = 5
+    wl = synth.small_workload(batch=3, tq=tq, len_lo=70, len_hi=400, seed=141)
+    inp = make(wl)
+    dev = DevInputs(inp)
+    out, _ = run_decode(dev, splits=3)
+    got = bf16_to_f64(out)
+    for i in range(tq):
+        lens_i = torch.tensor(inp.seq_lens - (tq - 1 - i), dtype=torch.int32, device="cuda")
+        single = api.decode_step(dev.q_c[:, i:i + 1].contiguous(), dev.q_r[:, i:i + 1].contiguous(),
+                                 dev.kv, dev.table, lens_i, dev.w_uk, dev.w_uv, wl.scale, splits=3)
+        torch.cuda.synchronize()
+        d = bf16_to_f64(single)[:, 0]
+        assert np.max(np.abs(d - got[:, i])) <= 1e-2, i
+
+
 @pytest.mark.parametrize("tq,lens", [
     (1, [1, 2, 63, 64, 65, 128, 129, 191]),
     (2, [2, 3, 64, 65, 66, 127, 128, 129]),
+    (8, [8, 9, 63, 64, 65, 71, 72, 136]),
 ])
 def test_edge_lengths(tq, lens):
     print(f"[case] edge lengths tq={tq} lens={lens}", flush=True)

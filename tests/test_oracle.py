@@ -70,6 +70,22 @@ def test_hand_case_two_queries_causal(form):
 
 
 @pytest.mark.parametrize("form", ["unabsorbed", "absorbed"])
+def test_hand_case_three_queries_causal(form):
+    # Tq = L = 3 (a token and two drafts): query i sits at position i.
+    out, lse = oracle.decode(*_hand(tq=3), form=form)
+    # Query 0 sees token 0 alone: its value, v = 2 (head 0) and 1 (head 1), lse = its score.
+    assert out[0, 0, 0, 0] == pytest.approx(2.0, rel=1e-15)
+    assert out[0, 0, 1, 0] == pytest.approx(1.0, rel=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(1.0, rel=1e-15)
+    assert lse[0, 0, 1] == pytest.approx(0.0, abs=1e-15)
+    # Query 1 sees tokens 0 and 1, query 2 all three.
+    assert out[0, 1, 0, 0] == pytest.approx((2 * E + 3) / (E + 1), rel=1e-14)
+    assert out[0, 1, 1, 0] == pytest.approx(-math.tanh(1.0), rel=1e-14)
+    assert out[0, 2, 0, 0] == pytest.approx((7 * E + 3) / (2 * E + 1), rel=1e-14)
+    assert out[0, 2, 1, 0] == pytest.approx((1 - E**2) / (1 + E + E**2), rel=1e-14)
+
+
+@pytest.mark.parametrize("form", ["unabsorbed", "absorbed"])
 def test_hand_case_scaled(form):
     x = math.exp(1 / math.sqrt(2))
     out, _ = oracle.decode(*_hand(scale=1 / math.sqrt(2)), form=form)
