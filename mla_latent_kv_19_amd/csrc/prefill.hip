@@ -225,6 +225,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_attn_kernel(
   const int last_q = min(T - 1, qblk * 128 + 127);
   const int n_keys = L - T + last_q + 1;
   const int n_tiles = (n_keys + kKeyTile - 1) / kKeyTile;
+  // Position of this wave's first query if all 32 of its queries exist, else
+  // -1 (then every tile takes the masked path).
+  const int wave_q0 = qblk * 128 + 32 * wave;
+  const int wave_qmin = (wave_q0 + 31 < T) ? L - T + wave_q0 : -1;
 
   // Q^T as B operands: k-step ks covers dims 16ks .. of [q_C (128); q_R (64)].
   bf16x8 qreg[12];
@@ -279,18 +283,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_attn_kernel(
       }
     }
     // s[kt][r]: key k0 + 32kt + 8*(r/4) + 4*half + r%4, query qi.
+    // Raw scores; the scale (> 0) is applied inside the exponent below, so the
+    // maximum can be taken first.  Only tiles that reach past the wave's first
+    // query position need the per-element causal mask.
     float x[32];
     float mx = -INFINITY;
+    if (k0 + kKeyTile - 1 <= wave_qmin) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = q_ok && key <= qpos && key < L;
-        x[16 * kt + r] = vis ? s[kt][r] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[16 * kt + r]);
+      for (int r = 0; r < 32; ++r) {
+        x[r] = s[r >> 4][r & 15];
+        mx = fmaxf(mx, x[r]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = q_ok && key <= qpos && key < L;
+          x[16 * kt + r] = vis ? s[kt][r] : -INFINITY;
+          mx = fmaxf(mx, x[16 * kt + r]);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;      // log2 units
     const bool move = mx > m_ref + 8.f;
     if (move) {
       const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mx);
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_attn_kernel(
     bf16x8 pb[4];
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      const float p = fast_exp2(x[r] - m_use);
+      const float p = fast_exp2(fmaf(x[r], scale_log2, -m_use));
       l_run += p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
