@@ -48,14 +48,18 @@ __device__ __forceinline__ int vt_pos(int t) {
 // ===========================================================================
 constexpr int kWkPitch = 64 + 8;     // bf16 per W_UK LDS row (144 B)
 constexpr int kWvPitch = 128 + 24;   // bf16 per W_UV LDS row (304 B)
+constexpr int kWkSlice = 128 * kWkPitch;   // bf16 per W_UK slice buffer
+constexpr int kWvSlice = 64 * kWvPitch;    // bf16 per W_UV slice buffer
 
-__global__ __launch_bounds__(kPfThreads) void prefill_kv_kernel(
+// Two work-groups per CU (two waves per SIMD) so one hides the other's waits;
+// the weight slices are double buffered through registers.
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ w_uk,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_vt,
     int max_blocks, int n_tblk) {
-  __shared__ __attribute__((aligned(16))) uint16_t wk[128 * kWkPitch];   // [i][j slice]
-  __shared__ __attribute__((aligned(16))) uint16_t wv[64 * kWvPitch];    // [j slice][d]
+  __shared__ __attribute__((aligned(16))) uint16_t wk[2 * kWkSlice];   // [i][j slice] x 2
+  __shared__ __attribute__((aligned(16))) uint16_t wv[2 * kWvSlice];   // [j slice][d] x 2
 
   const int tblk = blockIdx.x % n_tblk;
   const int h = (blockIdx.x / n_tblk) % 128;
@@ -81,49 +85,91 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kv_kernel(
 
   const uint16_t* wuk = w_uk + (size_t)h * 128 * 512;
   const uint16_t* wuv = w_uv + (size_t)h * 512 * 128;
-  const lds_u8* wk_l = to_lds(wk);
-  const lds_u8* wv_l = to_lds(wv);
   // B operand for K_C (W_UK^T: k = j, n = i): lane reads row i = 32n + l32,
   // 8 consecutive j at 16*ks + 8*half.
-  const lds_u8* wk_rd = wk_l + (l32 * kWkPitch + 8 * half) * 2;
+  const int wk_rd = (l32 * kWkPitch + 8 * half) * 2;
   // B operand for V (W_UV: k = j, n = d) by transposed reads: group g = lane/16
   // supplies rows j = 16*ks + 8*(g/2) + q/4 (+4), columns 32n + 16*(g%2) + 4*(q%4).
-  const lds_u8* wv_rd = wv_l + ((8 * half + (q16 >> 2)) * kWvPitch + 16 * colhalf + 4 * (q16 & 3)) * 2;
+  const int wv_rd = ((8 * half + (q16 >> 2)) * kWvPitch + 16 * colhalf + 4 * (q16 & 3)) * 2;
 
+  // Slice jc (j = 64jc .. 64jc+63) of both weights: 8 sixteen-byte chunks per
+  // thread, global -> registers -> LDS.  Thread chunk k: W_UK row (ch / 8),
+  // W_UV row (ch / 16), ch = 256k + tid.
+  const uint16_t* wk_src[4];
+  const uint16_t* wv_src[4];
+  int wk_dst[4], wv_dst[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int ch = k * kPfThreads + tid;
+    wk_src[k] = wuk + (size_t)(ch >> 3) * 512 + (ch & 7) * 8;
+    wv_src[k] = wuv + (size_t)(ch >> 4) * 128 + (ch & 15) * 8;
+    wk_dst[k] = (ch >> 3) * kWkPitch + (ch & 7) * 8;
+    wv_dst[k] = (ch >> 4) * kWvPitch + (ch & 15) * 8;
+  }
+  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+#define MLA_PF_LOAD_SLICE(jc)                                                       \
+  do {                                                                              \
+    sk0 = *reinterpret_cast<const uint4*>(wk_src[0] + 64 * (jc));                   \
+    sk1 = *reinterpret_cast<const uint4*>(wk_src[1] + 64 * (jc));                   \
+    sk2 = *reinterpret_cast<const uint4*>(wk_src[2] + 64 * (jc));                   \
+    sk3 = *reinterpret_cast<const uint4*>(wk_src[3] + 64 * (jc));                   \
+    sv0 = *reinterpret_cast<const uint4*>(wv_src[0] + (size_t)64 * 128 * (jc));     \
+    sv1 = *reinterpret_cast<const uint4*>(wv_src[1] + (size_t)64 * 128 * (jc));     \
+    sv2 = *reinterpret_cast<const uint4*>(wv_src[2] + (size_t)64 * 128 * (jc));     \
+    sv3 = *reinterpret_cast<const uint4*>(wv_src[3] + (size_t)64 * 128 * (jc));     \
+  } while (0)
+#define MLA_PF_STORE_SLICE(buf)                                                     \
+  do {                                                                              \
+    uint16_t* wkb = wk + (buf) * kWkSlice;                                          \
+    uint16_t* wvb = wv + (buf) * kWvSlice;                                          \
+    *reinterpret_cast<uint4*>(wkb + wk_dst[0]) = sk0;                               \
+    *reinterpret_cast<uint4*>(wkb + wk_dst[1]) = sk1;                               \
+    *reinterpret_cast<uint4*>(wkb + wk_dst[2]) = sk2;                               \
+    *reinterpret_cast<uint4*>(wkb + wk_dst[3]) = sk3;                               \
+    *reinterpret_cast<uint4*>(wvb + wv_dst[0]) = sv0;                               \
+    *reinterpret_cast<uint4*>(wvb + wv_dst[1]) = sv1;                               \
+    *reinterpret_cast<uint4*>(wvb + wv_dst[2]) = sv2;                               \
+    *reinterpret_cast<uint4*>(wvb + wv_dst[3]) = sv3;                               \
+  } while (0)
+
+  bf16x8 a[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) a[ks] = ld_global_bf16x8(crow + 16 * ks);
+  MLA_PF_LOAD_SLICE(0);
+  MLA_PF_STORE_SLICE(0);
+#pragma unroll
   for (int jc = 0; jc < 8; ++jc) {
-    __syncthreads();
-    // W_UK[h][0:128][64jc : +64] -> wk: 128 rows x 8 chunks.
+    // The next slice's weights and latent operands are in flight meanwhile.
+    bf16x8 an[4];
+    if (jc + 1 < 8) {
+      MLA_PF_LOAD_SLICE(jc + 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int ch = k * kPfThreads + tid;
-      const int i = ch >> 3, c = ch & 7;
-      *reinterpret_cast<uint4*>(&wk[i * kWkPitch + c * 8]) =
-          *reinterpret_cast<const uint4*>(wuk + (size_t)i * 512 + 64 * jc + c * 8);
+      for (int ks = 0; ks < 4; ++ks) an[ks] = ld_global_bf16x8(crow + 64 * (jc + 1) + 16 * ks);
     }
-    // W_UV[h][64jc : +64][0:128] -> wv: 64 rows x 16 chunks.
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int ch = k * kPfThreads + tid;
-      const int j = ch >> 4, c = ch & 15;
-      *reinterpret_cast<uint4*>(&wv[j * kWvPitch + c * 8]) =
-          *reinterpret_cast<const uint4*>(wuv + (size_t)(64 * jc + j) * 128 + c * 8);
-    }
-    bf16x8 a[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = ld_global_bf16x8(crow + 64 * jc + 16 * ks);
-    __syncthreads();
+    __syncthreads();                             // slice jc visible in buffer jc % 2
+    const lds_u8* wk_l = to_lds(wk + (jc & 1) * kWkSlice) + wk_rd;
+    const lds_u8* wv_l = to_lds(wv + (jc & 1) * kWvSlice) + wv_rd;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const bf16x8 bk = ld_lds_bf16x8(wk_rd + (32 * n * kWkPitch + 16 * ks) * 2);
+        const bf16x8 bk = ld_lds_bf16x8(wk_l + (32 * n * kWkPitch + 16 * ks) * 2);
         acc_k[n] = mfma32(a[ks], bk, acc_k[n]);
-        const bf16x4 lo = ld_lds_tr(wv_rd + ((16 * ks) * kWvPitch + 32 * n) * 2);
-        const bf16x4 hi = ld_lds_tr(wv_rd + ((16 * ks + 4) * kWvPitch + 32 * n) * 2);
+        const bf16x4 lo = ld_lds_tr(wv_l + ((16 * ks) * kWvPitch + 32 * n) * 2);
+        const bf16x4 hi = ld_lds_tr(wv_l + ((16 * ks + 4) * kWvPitch + 32 * n) * 2);
         acc_v[n] = mfma32(a[ks], cat(lo, hi), acc_v[n]);
       }
     }
+    if (jc + 1 < 8) {
+      // Buffer (jc+1) % 2 was last read in iteration jc-1, before this
+      // iteration's barrier.
+      MLA_PF_STORE_SLICE((jc + 1) & 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a[ks] = an[ks];
+    }
   }
+#undef MLA_PF_LOAD_SLICE
+#undef MLA_PF_STORE_SLICE
 
   // acc[n][r]: token t0 + 32*wave + 8*(r/4) + 4*half + r%4, column 32n + l32.
   uint16_t* kdst = ws_k + ((size_t)(b * 128 + h) * Lpad) * 128;
