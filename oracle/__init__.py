@@ -34,9 +34,18 @@ Pin status (what fixes each function other than itself):
   all-empty convention.
 * ``split_partial`` -- the same partition property.
 
+Cache append (``oracle.cache_append``): kv_down, RMSNorm, RoPE and the paged
+write of new tokens ("DeepSeek-V3" llm-vis explorer, boxes "KV latent
+compression" and "Rotary position embedding (RoPE)").  Pins: RoPE hand cases
+with closed forms, the inverse frequencies, position 0, pair norms, relative
+position and composition identities; RMSNorm hand cases, scale invariance and
+unit RMS; kv_down against brute force and coordinate-selecting weights; the
+split order and the page placement worked out by hand.
+
 No function is "parity unpinned".
 """
 
+from . import cache_append  # noqa: F401
 from .mla_oracle import (  # noqa: F401
     absorb_q,
     attend_absorbed,

@@ -1,0 +1,109 @@
+"""Pins of the cache-append oracle (kv_down -> RMSNorm | RoPE -> paged write).
+
+Each test checks the oracle against something other than itself: a hand case
+with a closed form, an identity rotations or norms must satisfy, brute force
+on a tiny input, or a placement worked out by hand.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import cache_append as ca
+
+
+def test_rope_hand_cases():
+    # d_r = 2: one pair, inv_freq = [1]: a rotation by pos radians.
+    np.testing.assert_allclose(ca.apply_rope([1.0, 0.0], 1, 10000.0),
+                               [math.cos(1.0), math.sin(1.0)], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(ca.apply_rope([0.0, 1.0], 2, 10000.0),
+                               [-math.sin(2.0), math.cos(2.0)], rtol=0, atol=1e-15)
+    # d_r = 4, theta = 16: inv_freq = [1, 1/4]; pair 1 of (0, 0, 2, 0) at pos 2 turns by 1/2.
+    np.testing.assert_allclose(ca.apply_rope([0.0, 0.0, 2.0, 0.0], 2, 16.0),
+                               [0.0, 0.0, 2 * math.cos(0.5), 2 * math.sin(0.5)], atol=1e-15)
+
+
+def test_rope_inverse_frequencies():
+    inv = ca.rope_inv_freq(64, 10000.0)
+    assert inv.shape == (32,)
+    assert inv[0] == 1.0
+    assert inv[1] == pytest.approx(math.exp(-math.log(10000.0) / 32), rel=1e-15)
+    assert inv[31] == pytest.approx(10000.0 ** (-62 / 64), rel=1e-14)
+    assert np.all(np.diff(inv) < 0)
+
+
+def test_rope_rotation_properties():
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    # Position 0 is the identity; each pair keeps its length.
+    np.testing.assert_array_equal(ca.apply_rope(q, 0, 10000.0), q)
+    r = ca.apply_rope(q, 12345, 10000.0)
+    np.testing.assert_allclose(r[0::2] ** 2 + r[1::2] ** 2, q[0::2] ** 2 + q[1::2] ** 2, rtol=1e-12)
+    # Scores depend on the relative position only; rotations compose.
+    for m, n in [(7, 3), (1000, 999), (163839, 5)]:
+        lhs = ca.apply_rope(q, m, 10000.0) @ ca.apply_rope(k, n, 10000.0)
+        rhs = ca.apply_rope(q, m - n, 10000.0) @ k
+        assert lhs == pytest.approx(rhs, rel=1e-9, abs=1e-9)
+    np.testing.assert_allclose(ca.apply_rope(ca.apply_rope(q, 40, 10000.0), 2, 10000.0),
+                               ca.apply_rope(q, 42, 10000.0), rtol=1e-12, atol=1e-12)
+
+
+def test_rms_norm_hand_case_and_invariances():
+    # (3, 4): mean square 12.5.
+    np.testing.assert_allclose(ca.rms_norm([3.0, 4.0], [1.0, 1.0], 0.0),
+                               [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=1e-15)
+    np.testing.assert_allclose(ca.rms_norm([3.0, 4.0], [2.0, -1.0], 0.0),
+                               [6 / math.sqrt(12.5), -4 / math.sqrt(12.5)], rtol=1e-15)
+    # eps keeps a zero vector at zero; with eps the hand case shifts by it.
+    np.testing.assert_array_equal(ca.rms_norm([0.0, 0.0], [1.0, 1.0], 1e-6), [0.0, 0.0])
+    np.testing.assert_allclose(ca.rms_norm([3.0, 4.0], [1.0, 1.0], 0.5),
+                               [3 / math.sqrt(13.0), 4 / math.sqrt(13.0)], rtol=1e-15)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(512)
+    y = ca.rms_norm(x, np.ones(512), 0.0)
+    assert np.sqrt(np.mean(y * y)) == pytest.approx(1.0, rel=1e-14)
+    np.testing.assert_allclose(ca.rms_norm(5.0 * x, np.ones(512), 0.0), y, rtol=1e-13)
+
+
+def test_kv_down_against_brute_force():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 7))
+    w = rng.standard_normal((5, 7))
+    got = ca.kv_down(x, w)
+    for m in range(3):
+        for o in range(5):
+            assert got[m, o] == pytest.approx(sum(x[m, j] * w[o, j] for j in range(7)), rel=1e-13)
+    # A weight of unit rows picks coordinates.
+    sel = np.eye(7)[[6, 0, 3]]
+    np.testing.assert_array_equal(ca.kv_down(x, sel), x[:, [6, 0, 3]])
+
+
+def test_cache_rows_split_order():
+    # d_model = 4, d_c = 2, d_r = 2: outputs 0,1 are the latent, 2,3 the rotary key.
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    w = np.eye(4)[[0, 1, 2, 3]]
+    rows = ca.cache_rows(x, w, gamma=[1.0, 1.0], positions=[1], eps=0.0, theta=10000.0, d_c=2)
+    np.testing.assert_allclose(rows[0, :2], [1 / math.sqrt(2.5), 2 / math.sqrt(2.5)], rtol=1e-15)
+    np.testing.assert_allclose(rows[0, 2:], [3 * math.cos(1) - 4 * math.sin(1),
+                                             3 * math.sin(1) + 4 * math.cos(1)], rtol=1e-14)
+
+
+def test_cache_append_placement():
+    # Two sequences, block size 4; sequence 0 owns blocks [2, 0], sequence 1 [1].
+    kv = np.full((3, 4, 4), np.nan)
+    table = np.array([[2, 0], [1, -1]], dtype=np.int32)
+    x = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [0, 0, 1.0, 0]])
+    w = np.eye(4)
+    out, rows = ca.cache_append(x, w, [1.0, 1.0], seq_idx=[0, 1, 0], positions=[5, 2, 0],
+                                block_table=table, kv_cache=kv, eps=1e-6, theta=10000.0, d_c=2)
+    np.testing.assert_array_equal(out[0, 1], rows[0])      # seq 0, pos 5 -> block 0, row 1
+    np.testing.assert_array_equal(out[1, 2], rows[1])      # seq 1, pos 2 -> block 1, row 2
+    np.testing.assert_array_equal(out[2, 0], rows[2])      # seq 0, pos 0 -> block 2, row 0
+    written = {(0, 1), (1, 2), (2, 0)}
+    for blk in range(3):
+        for r in range(4):
+            if (blk, r) not in written:
+                assert np.all(np.isnan(out[blk, r]))
+    # The input cache is left as it was.
+    assert np.all(np.isnan(kv))
