@@ -145,6 +145,39 @@ int mla_prefill(const uint16_t* q_c, const uint16_t* q_r,
                 int num_blocks, int block_size, int max_blocks_per_seq,
                 float softmax_scale, void* stream);
 
+/*
+ * Cache append ("DeepSeek-V3" llm-vis explorer, boxes "KV latent compression"
+ * and "Rotary position embedding (RoPE)"): for each of M new tokens m, with
+ * hidden state x[m], sequence seq_idx[m] and position positions[m],
+ *   [c_raw | k_raw] = w_kv x[m]                      (d_model -> d_c + d_r)
+ *   c   = c_raw / sqrt(mean(c_raw^2) + eps) * gamma   (RMSNorm over d_c)
+ *   k_R = (k_raw[2i], k_raw[2i+1]) rotated by positions[m] * theta^(-2i/d_r)
+ * is written as the cache row c | k_R of that token: block
+ * block_table[seq_idx[m], positions[m] / block_size], row
+ * positions[m] % block_size.  Only those M rows are written.
+ * x       bf16 [M, d_model]
+ * w_kv    bf16 [d_c + d_r, d_model]   (a linear layer's [out, in] weight)
+ * gamma   bf16 [d_c]                  RMSNorm gain
+ * seq_idx, positions  int32 [M]      device arrays, not validated (a sync):
+ *         0 <= seq_idx < (rows of block_table), 0 <= positions <
+ *         max_blocks_per_seq * block_size, the block named for the position
+ *         in range; two tokens of one call must not share a cache row.
+ * kv_cache  as described above; rows written in bf16, rounded to nearest even
+ * workspace fp32, at least mla_cache_append_workspace_bytes(M, d_model) bytes,
+ *         256-byte aligned: the K-sliced partial products.
+ * Supported: d_c = 512, d_r = 64, block_size = 64, d_model a multiple of 16
+ * (7168 in DeepSeek-V3).  theta > 0 (10000 in DeepSeek-V3), eps >= 0.
+ */
+int mla_cache_append(const uint16_t* x, const uint16_t* w_kv, const uint16_t* gamma,
+                     const int32_t* seq_idx, const int32_t* positions,
+                     const int32_t* block_table, uint16_t* kv_cache,
+                     void* workspace, size_t workspace_bytes,
+                     int M, int d_model, int d_c, int d_r, int num_blocks, int block_size,
+                     int max_blocks_per_seq, float eps, float rope_theta, void* stream);
+
+/* Workspace bytes mla_cache_append needs for M tokens (0 on invalid args). */
+size_t mla_cache_append_workspace_bytes(int M, int d_model);
+
 /* Bytes of part_o plus part_lse for one decode step (two separate buffers). */
 size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits);
 size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits);

@@ -26,7 +26,8 @@ H, D_C, D_R, D_H, D_V, BLOCK = 128, 512, 64, 128, 128, 64
 EXPORTED = (
     "mla_strerror", "mla_version", "mla_absorb_q", "mla_decode_paged", "mla_combine",
     "mla_prefill", "mla_decode_part_o_bytes", "mla_decode_part_lse_bytes",
-    "mla_prefill_workspace_bytes", "mla_decode_num_splits",
+    "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
+    "mla_cache_append_workspace_bytes",
 )
 
 
@@ -65,6 +66,10 @@ def load():
     lib.mla_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_prefill_workspace_bytes.restype = Z
     lib.mla_decode_num_splits.argtypes, lib.mla_decode_num_splits.restype = [I, I, I, I, I, I], I
+    lib.mla_cache_append.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, F, P]
+    lib.mla_cache_append.restype = I
+    lib.mla_cache_append_workspace_bytes.argtypes = [I, I]
+    lib.mla_cache_append_workspace_bytes.restype = Z
     _lib = lib
     return lib
 
@@ -235,3 +240,36 @@ def prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale
         b, t, H, D_C, D_R, D_H, D_V, kv_cache.shape[0], BLOCK, block_table.shape[1],
         ctypes.c_float(softmax_scale), _stream(dev)))
     return out
+
+
+def cache_append_workspace_bytes(m, d_model):
+    return load().mla_cache_append_workspace_bytes(m, d_model)
+
+
+def cache_append(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache, eps=1e-6,
+                 rope_theta=10000.0, workspace=None):
+    """Write the cache rows (RMSNorm(latent) | RoPE(rotary key)) of M new tokens.
+
+    x [M, d_model] bf16, w_kv [576, d_model] bf16, gamma [512] bf16, seq_idx and
+    positions [M] int32; kv_cache is updated in place.
+    """
+    m, d_model = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(w_kv, "w_kv", torch.bfloat16, (D_C + D_R, d_model))
+    _need(gamma, "gamma", torch.bfloat16, (D_C,))
+    _need(seq_idx, "seq_idx", torch.int32, (m,))
+    _need(positions, "positions", torch.int32, (m,))
+    _need(block_table, "block_table", torch.int32)
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    nbytes = cache_append_workspace_bytes(m, d_model)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"cache append workspace needs {nbytes} bytes")
+    dev = _same_device(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache, workspace)
+    _check("mla_cache_append", load().mla_cache_append(
+        _ptr(x), _ptr(w_kv), _ptr(gamma), _ptr(seq_idx), _ptr(positions), _ptr(block_table),
+        _ptr(kv_cache), _ptr(workspace), workspace.numel(), m, d_model, D_C, D_R,
+        kv_cache.shape[0], BLOCK, block_table.shape[1], ctypes.c_float(eps),
+        ctypes.c_float(rope_theta), _stream(dev)))
+    return kv_cache

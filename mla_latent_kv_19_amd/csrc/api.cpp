@@ -26,12 +26,21 @@ extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_
                                          int B, int T, int max_blocks, float softmax_scale,
                                          hipStream_t stream);
 
+extern "C" int mla_append_splits(int M, int d_model);
+extern "C" hipError_t mla_launch_cache_append(const uint16_t* x, const uint16_t* w_kv,
+                                              const uint16_t* gamma, const int32_t* seq_idx,
+                                              const int32_t* positions, const int32_t* block_table,
+                                              uint16_t* kv, float* workspace, int M, int d_model,
+                                              int max_blocks, float eps, float theta,
+                                              hipStream_t stream);
+
 namespace {
 
 // The one shape family the kernels are written for (DeepSeek-V3's MLA dims).
 constexpr int kH = 128, kDC = 512, kDR = 64, kDH = 128, kDV = 128, kBlock = 64;
 constexpr int kMaxTq = 8;             // query tokens per sequence in one decode call
 constexpr int kMaxRows = 65536;
+constexpr int kMaxAppendRows = 1 << 20;    // new tokens per cache-append call
 
 int status_of(hipError_t e) {
   if (e == hipSuccess) return MLA_OK;
@@ -131,6 +140,31 @@ int mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv_cac
   return status_of(mla_launch_prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, out,
                                       workspace, B, T, max_blocks_per_seq, softmax_scale,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_cache_append_workspace_bytes(int M, int d_model) {
+  if (M <= 0 || d_model <= 0 || d_model % 16 != 0 || M > kMaxAppendRows) return 0;
+  return (size_t)mla_append_splits(M, d_model) * M * (kDC + kDR) * sizeof(float);
+}
+
+int mla_cache_append(const uint16_t* x, const uint16_t* w_kv, const uint16_t* gamma,
+                     const int32_t* seq_idx, const int32_t* positions, const int32_t* block_table,
+                     uint16_t* kv_cache, void* workspace, size_t workspace_bytes, int M,
+                     int d_model, int d_c, int d_r, int num_blocks, int block_size,
+                     int max_blocks_per_seq, float eps, float rope_theta, void* stream) {
+  if (!x || !w_kv || !gamma || !seq_idx || !positions || !block_table || !kv_cache || !workspace)
+    return MLA_ERR_INVALID_ARG;
+  if (M <= 0 || M > kMaxAppendRows || d_model <= 0 || d_c <= 0 || d_r <= 0 || num_blocks <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || !std::isfinite(eps) || eps < 0.f ||
+      !finite_positive(rope_theta) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d_c != kDC || d_r != kDR || block_size != kBlock || d_model % 16 != 0)
+    return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < mla_cache_append_workspace_bytes(M, d_model)) return MLA_ERR_INVALID_ARG;
+  return status_of(mla_launch_cache_append(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache,
+                                           static_cast<float*>(workspace), M, d_model,
+                                           max_blocks_per_seq, eps, rope_theta,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size, int num_cus) {

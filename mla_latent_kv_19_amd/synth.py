@@ -232,3 +232,48 @@ def make_inputs(wl, seq_lens=None):
 def small_workload(name="small", batch=3, tq=1, len_lo=1, len_hi=300, seed=7, **kw):
     """A reduced-size workload with the full per-head dims, for quick parity checks."""
     return Workload(name, batch=batch, tq=tq, len_lo=len_lo, len_hi=len_hi, seed=seed, **kw)
+
+
+@dataclass
+class AppendInputs:
+    """Inputs of one cache append (bf16 bit arrays and int32 index arrays)."""
+
+    x: np.ndarray            # [M, d_model]
+    w_kv: np.ndarray         # [d_c + d_r, d_model]
+    gamma: np.ndarray        # [d_c]
+    seq_idx: np.ndarray      # [M]
+    positions: np.ndarray    # [M]
+    block_table: np.ndarray  # [n_seq, max_blocks]
+    kv_cache: np.ndarray     # [num_blocks, block_size, d_c + d_r], bf16 NaN everywhere
+
+
+def append_inputs(m, d_model=7168, n_seq=4, max_pos=163840, seed=2001, block_size=64,
+                  d_c=512, d_r=64, spare_frac=0.1):
+    """M new tokens spread over n_seq sequences at distinct positions below max_pos.
+
+    Hidden states are N(0, 1); the kv_down weight is N(0, 1/d_model) so each
+    projected value is about N(0, 1); the RMSNorm gain is 1 + N(0, 0.1^2).
+    Every sequence owns ceil(max_pos / block_size) pages of a pool with spare
+    pages, assigned by a seeded permutation; the cache starts as bf16 NaN, so
+    any row the append does not own stays NaN.
+    """
+    names = ["x", "w", "gamma", "seq", "pos", "table"]
+    s = dict(zip(names, np.random.SeedSequence(seed).spawn(len(names))))
+    x = _normal_bf16(s["x"], (m, d_model))
+    w_kv = _normal_bf16(s["w"], (d_c + d_r, d_model), 1.0 / np.sqrt(d_model))
+    g = np.random.Generator(np.random.PCG64(s["gamma"]))
+    gamma = f32_to_bf16_bits(1.0 + 0.1 * g.standard_normal(d_c, dtype=np.float32))
+    rng = np.random.Generator(np.random.PCG64(s["seq"]))
+    seq_idx = rng.integers(0, n_seq, size=m).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(s["pos"]))
+    positions = np.empty(m, dtype=np.int32)
+    for b in range(n_seq):
+        idx = np.nonzero(seq_idx == b)[0]
+        positions[idx] = rng.choice(max_pos, size=idx.size, replace=False)
+    pages = (max_pos + block_size - 1) // block_size
+    total = n_seq * pages
+    num_blocks = total + int(np.ceil(spare_frac * total))
+    rng = np.random.Generator(np.random.PCG64(s["table"]))
+    table = rng.permutation(num_blocks)[:total].astype(np.int32).reshape(n_seq, pages)
+    kv = np.full((num_blocks, block_size, d_c + d_r), BF16_NAN, dtype=np.uint16)
+    return AppendInputs(x, w_kv, gamma, seq_idx, positions, table, kv)

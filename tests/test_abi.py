@@ -126,3 +126,42 @@ def test_workspace_sizes_and_split_heuristic():
     assert lib.mla_decode_num_splits(1, 1, 128, 1024, 64, 256) == 16
     assert lib.mla_decode_num_splits(1, 1, 128, 1, 64, 256) == 1
     assert lib.mla_decode_num_splits(0, 1, 128, 1, 64, 256) == 0
+
+
+def _append(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, gamma=FAKE, seq=FAKE, pos=FAKE, table=FAKE, kv=FAKE,
+             ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40, M=4, d_model=7168, d_c=512, d_r=64,
+             num_blocks=10, block_size=64, max_blocks=4, eps=1e-6, theta=10000.0)
+    a.update(kw)
+    return lib.mla_cache_append(a["x"], a["w"], a["gamma"], a["seq"], a["pos"], a["table"],
+                                a["kv"], a["ws"], a["ws_bytes"], a["M"], a["d_model"], a["d_c"],
+                                a["d_r"], a["num_blocks"], a["block_size"], a["max_blocks"],
+                                ctypes.c_float(a["eps"]), ctypes.c_float(a["theta"]), NULL)
+
+
+def test_cache_append_argument_errors():
+    lib = _lib()
+    E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
+    assert _append(lib, x=NULL) == E
+    assert _append(lib, pos=NULL) == E
+    assert _append(lib, M=0) == E
+    assert _append(lib, eps=-1.0) == E
+    assert _append(lib, eps=float("inf")) == E
+    assert _append(lib, theta=0.0) == E
+    assert _append(lib, ws=ctypes.c_void_p(0x100010)) == E      # not 256-byte aligned
+    assert _append(lib, ws_bytes=16) == E
+    assert _append(lib, d_c=256) == U
+    assert _append(lib, d_r=32) == U
+    assert _append(lib, block_size=32) == U
+    assert _append(lib, d_model=7000) == U                      # not a multiple of 16
+
+
+def test_cache_append_workspace_bytes():
+    lib = _lib()
+    assert lib.mla_cache_append_workspace_bytes(0, 7168) == 0
+    assert lib.mla_cache_append_workspace_bytes(4, 7000) == 0
+    # One token: the K split fills the chip, each slice a [1, 576] fp32 partial.
+    one = lib.mla_cache_append_workspace_bytes(1, 7168)
+    assert one % (576 * 4) == 0 and 1 <= one // (576 * 4) <= 7168 // 16
+    # Many tokens: no split needed.
+    assert lib.mla_cache_append_workspace_bytes(4096, 7168) == 4096 * 576 * 4
