@@ -152,6 +152,49 @@ def bench_prefill(steps, warmup):
             "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flop": flops}
 
 
+def bench_append(steps, warmup):
+    """Cache append (kv_down 7168 -> 576, RMSNorm, RoPE, paged write) for the
+    64 new tokens of one decode step and for a 4096-token prefill chunk."""
+    import torch
+    from mla_latent_kv_19_amd import api, synth
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    res = {}
+    for m, n_seq, max_pos in ((64, 64, 128), (4096, 1, 4096)):
+        a = synth.append_inputs(m, n_seq=n_seq, max_pos=max_pos, seed=2300 + m)
+        x, w, g, kv = dev(a.x), dev(a.w_kv), dev(a.gamma), dev(a.kv_cache)
+        seq = torch.from_numpy(a.seq_idx).cuda()
+        pos = torch.from_numpy(a.positions).cuda()
+        table = torch.from_numpy(a.block_table).cuda()
+        ws = torch.empty(api.cache_append_workspace_bytes(m, 7168), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            api.cache_append(x, w, g, seq, pos, table, kv, workspace=ws)
+
+        for _ in range(warmup):
+            run()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            run()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        flop = 2.0 * m * 7168 * 576
+        hbm = 576 * 7168 * 2 + m * 7168 * 2 + m * 576 * 2 + 512 * 2      # weight, x, rows, gain
+        res[f"tokens_{m}"] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+                              "gbs": hbm / (ms * 1e-3) / 1e9,
+                              "bound": "hbm" if m <= 256 else "mfma",
+                              "frac": (hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS) if m <= 256
+                              else (flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -290,6 +333,7 @@ def main():
         "input_gen_s": gen_s,
     }
     res["prefill"] = bench_prefill(max(3, args.steps // 4), 2)
+    res["cache_append"] = bench_append(max(5, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, meta, args.cpu_seconds)
     else:

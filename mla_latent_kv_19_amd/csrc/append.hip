@@ -14,7 +14,7 @@
 //   * append_gemm_kernel: one wave per (64 tokens, 64 outputs, K slice); A
 //     (hidden states) and B (weight rows, the layer's [out, in] layout) are
 //     both k-contiguous, so each MFMA 32x32x16 operand is one 16-byte load
-//     per lane straight from global memory, two k-steps in flight; fp32
+//     per lane straight from global memory, four k-steps in flight; fp32
 //     partial sums per K slice go to the workspace.  The K split is chosen so
 //     that a handful of decode tokens still spreads the 8 MB weight over the
 //     whole chip.
@@ -58,8 +58,11 @@ __global__ __launch_bounds__(64) void append_gemm_kernel(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  // Operands of k-step ks: a[0..1], b[0..1]; three register stages.
-  bf16x8 op[3][4];
+  // Operands of k-step ks: a[0..1], b[0..1]; five register stages, four
+  // k-steps of loads in flight (a K slice is often only 8 k-steps long, so
+  // latency, not bandwidth, sets its time).
+  constexpr int kStages = 5, kAhead = 4;
+  bf16x8 op[kStages][4];
   auto load = [&](int stage, int ks) {
     op[stage][0] = ld_global_bf16x8(arow[0] + 16 * ks);
     op[stage][1] = ld_global_bf16x8(arow[1] + 16 * ks);
@@ -67,13 +70,14 @@ __global__ __launch_bounds__(64) void append_gemm_kernel(const uint16_t* __restr
     op[stage][3] = ld_global_bf16x8(brow[1] + 16 * ks);
   };
   const int n = ks1 - ks0;
-  if (n > 0) load(0, ks0);
-  if (n > 1) load(1, ks0 + 1);
-  for (int j = 0; j < n; j += 3) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+  for (int u = 0; u < kAhead; ++u)
+    if (u < n) load(u, ks0 + u);
+  for (int j = 0; j < n; j += kStages) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) {
       if (j + u < n) {
-        if (j + u + 2 < n) load((u + 2) % 3, ks0 + j + u + 2);
+        if (j + u + kAhead < n) load((u + kAhead) % kStages, ks0 + j + u + kAhead);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -107,7 +111,22 @@ __global__ __launch_bounds__(64) void append_finish_kernel(
   float v[9];
 #pragma unroll
   for (int j = 0; j < 9; ++j) v[j] = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  // Slices in groups of 8, so that 72 loads are in flight at once.
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float t[8][9];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* p = part + ((size_t)(s + u) * M + m) * kAppOut + lane;
+#pragma unroll
+      for (int j = 0; j < 9; ++j) t[u][j] = p[64 * j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < 9; ++j) v[j] += t[u][j];
+  }
+  for (; s < splits; ++s) {
     const float* p = part + ((size_t)s * M + m) * kAppOut + lane;
 #pragma unroll
     for (int j = 0; j < 9; ++j) v[j] += p[64 * j];
