@@ -178,6 +178,44 @@ int mla_cache_append(const uint16_t* x, const uint16_t* w_kv, const uint16_t* ga
 /* Workspace bytes mla_cache_append needs for M tokens (0 on invalid args). */
 size_t mla_cache_append_workspace_bytes(int M, int d_model);
 
+/*
+ * Query side ("DeepSeek-V3" llm-vis explorer, "Query low-rank projection";
+ * "Teardown: DeepSeek-V3", section 4, c_q = W_DQ h, q_C = W_UQ c_q): for each
+ * of M tokens with hidden state x[m] at position positions[m],
+ *   c_q = w_dq x[m]  (d_model -> q_rank), c_q' = RMSNorm(c_q) * gamma_q,
+ *   per head h: [q_C | q_R'] = (w_uq c_q')[192h .. 192h + 191]  (d_h | d_r),
+ *   q_R = q_R' with pairs (2i, 2i+1) rotated by positions[m] * theta^(-2i/d_r).
+ * x bf16 [M, d_model]; w_dq bf16 [q_rank, d_model]; gamma_q bf16 [q_rank];
+ * w_uq bf16 [H * (d_h + d_r), q_rank]; positions int32 [M] (device, >= 0);
+ * q_c bf16 [M, H, d_h] and q_r bf16 [M, H, d_r] out (the inputs of
+ * mla_absorb_q and mla_decode_paged).  c_q' is rounded to bf16 between the
+ * two products.  workspace: mla_query_project_workspace_bytes(M, d_model,
+ * q_rank) bytes, 256-byte aligned.
+ * Supported: H = 128, d_h = 128, d_r = 64, d_model a multiple of 16, q_rank a
+ * multiple of 256 up to 4096 (7168 and 1536 in DeepSeek-V3).
+ */
+int mla_query_project(const uint16_t* x, const uint16_t* w_dq, const uint16_t* gamma_q,
+                      const uint16_t* w_uq, const int32_t* positions,
+                      uint16_t* q_c, uint16_t* q_r, void* workspace, size_t workspace_bytes,
+                      int M, int d_model, int q_rank, int H, int d_h, int d_r,
+                      float eps, float rope_theta, void* stream);
+size_t mla_query_project_workspace_bytes(int M, int d_model, int q_rank);
+
+/*
+ * Output projection ("DeepSeek-V3" llm-vis explorer, "Output projection": the
+ * concatenated value heads mapped back to the residual stream, no bias):
+ *   y[m] = w_o o[m]
+ * o bf16 [M, d_in] (mla_combine's out viewed as [M, H * d_v]); w_o bf16
+ * [d_out, d_in]; y bf16 [M, d_out] out, 8-byte aligned.  workspace:
+ * mla_output_project_workspace_bytes(M, d_in, d_out) bytes, 256-byte aligned.
+ * Supported: d_in a multiple of 16, d_out a multiple of 64 (16384 -> 7168 in
+ * DeepSeek-V3).
+ */
+int mla_output_project(const uint16_t* o, const uint16_t* w_o, uint16_t* y,
+                       void* workspace, size_t workspace_bytes,
+                       int M, int d_in, int d_out, void* stream);
+size_t mla_output_project_workspace_bytes(int M, int d_in, int d_out);
+
 /* Bytes of part_o plus part_lse for one decode step (two separate buffers). */
 size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits);
 size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits);

@@ -27,7 +27,8 @@ EXPORTED = (
     "mla_strerror", "mla_version", "mla_absorb_q", "mla_decode_paged", "mla_combine",
     "mla_prefill", "mla_decode_part_o_bytes", "mla_decode_part_lse_bytes",
     "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
-    "mla_cache_append_workspace_bytes",
+    "mla_cache_append_workspace_bytes", "mla_query_project", "mla_query_project_workspace_bytes",
+    "mla_output_project", "mla_output_project_workspace_bytes",
 )
 
 
@@ -70,6 +71,14 @@ def load():
     lib.mla_cache_append.restype = I
     lib.mla_cache_append_workspace_bytes.argtypes = [I, I]
     lib.mla_cache_append_workspace_bytes.restype = Z
+    lib.mla_query_project.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, F, F, P]
+    lib.mla_query_project.restype = I
+    lib.mla_query_project_workspace_bytes.argtypes = [I, I, I]
+    lib.mla_query_project_workspace_bytes.restype = Z
+    lib.mla_output_project.argtypes = [P, P, P, P, Z, I, I, I, P]
+    lib.mla_output_project.restype = I
+    lib.mla_output_project_workspace_bytes.argtypes = [I, I, I]
+    lib.mla_output_project_workspace_bytes.restype = Z
     _lib = lib
     return lib
 
@@ -273,3 +282,53 @@ def cache_append(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache, eps=
         kv_cache.shape[0], BLOCK, block_table.shape[1], ctypes.c_float(eps),
         ctypes.c_float(rope_theta), _stream(dev)))
     return kv_cache
+
+
+def query_project(x, w_dq, gamma_q, w_uq, positions, eps=1e-6, rope_theta=10000.0,
+                  q_c=None, q_r=None, workspace=None):
+    """(q_c [M, H, 128], q_r [M, H, 64]) bf16 of M tokens: W_DQ, RMSNorm, W_UQ, RoPE."""
+    m, d_model = x.shape
+    q_rank = w_dq.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(w_dq, "w_dq", torch.bfloat16, (q_rank, d_model))
+    _need(gamma_q, "gamma_q", torch.bfloat16, (q_rank,))
+    _need(w_uq, "w_uq", torch.bfloat16, (H * (D_H + D_R), q_rank))
+    _need(positions, "positions", torch.int32, (m,))
+    if q_c is None:
+        q_c = torch.empty((m, H, D_H), dtype=torch.bfloat16, device=x.device)
+    if q_r is None:
+        q_r = torch.empty((m, H, D_R), dtype=torch.bfloat16, device=x.device)
+    _need(q_c, "q_c", torch.bfloat16, (m, H, D_H))
+    _need(q_r, "q_r", torch.bfloat16, (m, H, D_R))
+    nbytes = load().mla_query_project_workspace_bytes(m, d_model, q_rank)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"query projection workspace needs {nbytes} bytes")
+    dev = _same_device(x, w_dq, gamma_q, w_uq, positions, q_c, q_r, workspace)
+    _check("mla_query_project", load().mla_query_project(
+        _ptr(x), _ptr(w_dq), _ptr(gamma_q), _ptr(w_uq), _ptr(positions), _ptr(q_c), _ptr(q_r),
+        _ptr(workspace), workspace.numel(), m, d_model, q_rank, H, D_H, D_R, ctypes.c_float(eps),
+        ctypes.c_float(rope_theta), _stream(dev)))
+    return q_c, q_r
+
+
+def output_project(o, w_o, y=None, workspace=None):
+    """y [M, d_out] bf16 = o [M, d_in] W_O^T."""
+    m, d_in = o.shape
+    d_out = w_o.shape[0]
+    _need(o, "o", torch.bfloat16)
+    _need(w_o, "w_o", torch.bfloat16, (d_out, d_in))
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.bfloat16, device=o.device)
+    _need(y, "y", torch.bfloat16, (m, d_out))
+    nbytes = load().mla_output_project_workspace_bytes(m, d_in, d_out)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=o.device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"output projection workspace needs {nbytes} bytes")
+    dev = _same_device(o, w_o, y, workspace)
+    _check("mla_output_project", load().mla_output_project(
+        _ptr(o), _ptr(w_o), _ptr(y), _ptr(workspace), workspace.numel(), m, d_in, d_out,
+        _stream(dev)))
+    return y

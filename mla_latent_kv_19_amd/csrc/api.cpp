@@ -26,13 +26,25 @@ extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_
                                          int B, int T, int max_blocks, float softmax_scale,
                                          hipStream_t stream);
 
-extern "C" int mla_append_splits(int M, int d_model);
+extern "C" int mla_linear_splits(int M, int N, int K);
 extern "C" hipError_t mla_launch_cache_append(const uint16_t* x, const uint16_t* w_kv,
                                               const uint16_t* gamma, const int32_t* seq_idx,
                                               const int32_t* positions, const int32_t* block_table,
                                               uint16_t* kv, float* workspace, int M, int d_model,
                                               int max_blocks, float eps, float theta,
                                               hipStream_t stream);
+
+extern "C" size_t mla_query_project_ws(int M, int d_model, int q_rank, int H);
+extern "C" hipError_t mla_launch_query_project(const uint16_t* x, const uint16_t* w_dq,
+                                               const uint16_t* gamma_q, const uint16_t* w_uq,
+                                               const int32_t* positions, uint16_t* q_c,
+                                               uint16_t* q_r, void* workspace, int M, int d_model,
+                                               int q_rank, int H, float eps, float theta,
+                                               hipStream_t stream);
+extern "C" size_t mla_output_project_ws(int M, int d_in, int d_out);
+extern "C" hipError_t mla_launch_output_project(const uint16_t* o, const uint16_t* w_o,
+                                                uint16_t* y, void* workspace, int M, int d_in,
+                                                int d_out, hipStream_t stream);
 
 namespace {
 
@@ -144,7 +156,7 @@ int mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv_cac
 
 size_t mla_cache_append_workspace_bytes(int M, int d_model) {
   if (M <= 0 || d_model <= 0 || d_model % 16 != 0 || M > kMaxAppendRows) return 0;
-  return (size_t)mla_append_splits(M, d_model) * M * (kDC + kDR) * sizeof(float);
+  return (size_t)mla_linear_splits(M, kDC + kDR, d_model) * M * (kDC + kDR) * sizeof(float);
 }
 
 int mla_cache_append(const uint16_t* x, const uint16_t* w_kv, const uint16_t* gamma,
@@ -165,6 +177,52 @@ int mla_cache_append(const uint16_t* x, const uint16_t* w_kv, const uint16_t* ga
                                            static_cast<float*>(workspace), M, d_model,
                                            max_blocks_per_seq, eps, rope_theta,
                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_query_project_workspace_bytes(int M, int d_model, int q_rank) {
+  if (M <= 0 || M > kMaxAppendRows || d_model <= 0 || d_model % 16 != 0 || q_rank <= 0 ||
+      q_rank % 256 != 0 || q_rank > 4096)
+    return 0;
+  return mla_query_project_ws(M, d_model, q_rank, kH);
+}
+
+int mla_query_project(const uint16_t* x, const uint16_t* w_dq, const uint16_t* gamma_q,
+                      const uint16_t* w_uq, const int32_t* positions, uint16_t* q_c, uint16_t* q_r,
+                      void* workspace, size_t workspace_bytes, int M, int d_model, int q_rank,
+                      int H, int d_h, int d_r, float eps, float rope_theta, void* stream) {
+  if (!x || !w_dq || !gamma_q || !w_uq || !positions || !q_c || !q_r || !workspace)
+    return MLA_ERR_INVALID_ARG;
+  if (M <= 0 || M > kMaxAppendRows || d_model <= 0 || q_rank <= 0 || H <= 0 || d_h <= 0 ||
+      d_r <= 0 || !std::isfinite(eps) || eps < 0.f || !finite_positive(rope_theta) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_h != kDH || d_r != kDR || d_model % 16 != 0 || q_rank % 256 != 0 ||
+      q_rank > 4096)
+    return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < mla_query_project_ws(M, d_model, q_rank, H)) return MLA_ERR_INVALID_ARG;
+  return status_of(mla_launch_query_project(x, w_dq, gamma_q, w_uq, positions, q_c, q_r, workspace,
+                                            M, d_model, q_rank, H, eps, rope_theta,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_output_project_workspace_bytes(int M, int d_in, int d_out) {
+  if (M <= 0 || M > kMaxAppendRows || d_in <= 0 || d_in % 16 != 0 || d_out <= 0 ||
+      d_out % 64 != 0)
+    return 0;
+  return mla_output_project_ws(M, d_in, d_out);
+}
+
+int mla_output_project(const uint16_t* o, const uint16_t* w_o, uint16_t* y, void* workspace,
+                       size_t workspace_bytes, int M, int d_in, int d_out, void* stream) {
+  if (!o || !w_o || !y || !workspace) return MLA_ERR_INVALID_ARG;
+  if (M <= 0 || M > kMaxAppendRows || d_in <= 0 || d_out <= 0 ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0 ||
+      (reinterpret_cast<uintptr_t>(y) & 7) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d_in % 16 != 0 || d_out % 64 != 0) return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < mla_output_project_ws(M, d_in, d_out)) return MLA_ERR_INVALID_ARG;
+  return status_of(mla_launch_output_project(o, w_o, y, workspace, M, d_in, d_out,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size, int num_cus) {

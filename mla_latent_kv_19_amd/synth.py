@@ -277,3 +277,28 @@ def append_inputs(m, d_model=7168, n_seq=4, max_pos=163840, seed=2001, block_siz
     table = rng.permutation(num_blocks)[:total].astype(np.int32).reshape(n_seq, pages)
     kv = np.full((num_blocks, block_size, d_c + d_r), BF16_NAN, dtype=np.uint16)
     return AppendInputs(x, w_kv, gamma, seq_idx, positions, table, kv)
+
+
+def query_inputs(m, d_model=7168, q_rank=1536, heads=128, d_h=128, d_r=64, max_pos=163840,
+                 seed=2401):
+    """(x, w_dq, gamma_q, w_uq, positions) for the query projection of m tokens.
+
+    x N(0, 1); w_dq N(0, 1/d_model) and w_uq N(0, 1/q_rank), so each product's
+    outputs are about N(0, 1); gamma_q 1 + N(0, 0.1^2); positions uniform
+    below max_pos.  bf16 bit arrays and int32 positions.
+    """
+    s = dict(zip(["x", "dq", "g", "uq", "pos"], np.random.SeedSequence(seed).spawn(5)))
+    x = _normal_bf16(s["x"], (m, d_model))
+    w_dq = _normal_bf16(s["dq"], (q_rank, d_model), 1.0 / np.sqrt(d_model))
+    g = np.random.Generator(np.random.PCG64(s["g"]))
+    gamma_q = f32_to_bf16_bits(1.0 + 0.1 * g.standard_normal(q_rank, dtype=np.float32))
+    w_uq = _normal_bf16(s["uq"], (heads * (d_h + d_r), q_rank), 1.0 / np.sqrt(q_rank))
+    rng = np.random.Generator(np.random.PCG64(s["pos"]))
+    positions = rng.integers(0, max_pos, size=m).astype(np.int32)
+    return x, w_dq, gamma_q, w_uq, positions
+
+
+def output_inputs(m, d_in=128 * 128, d_out=7168, seed=2501):
+    """(o, w_o): head outputs N(0, 1) and W_O N(0, 1/d_in), bf16 bit arrays."""
+    s = np.random.SeedSequence(seed).spawn(2)
+    return _normal_bf16(s[0], (m, d_in)), _normal_bf16(s[1], (d_out, d_in), 1.0 / np.sqrt(d_in))

@@ -42,10 +42,17 @@ position and composition identities; RMSNorm hand cases, scale invariance and
 unit RMS; kv_down against brute force and coordinate-selecting weights; the
 split order and the page placement worked out by hand.
 
+Projections (``oracle.projections``): the query side (W_DQ, RMSNorm, W_UQ,
+per-head split, RoPE of the rotary query) and the output projection W_O
+("Teardown: DeepSeek-V3" section 4; explorer "Query low-rank projection" and
+"Output projection").  Pins: a hand case through every step with closed-form
+values, position independence of q_C, position 0 leaving q_R unrotated, the
+per-head split order, brute force for W_O on tiny inputs.
+
 No function is "parity unpinned".
 """
 
-from . import cache_append  # noqa: F401
+from . import cache_append, projections  # noqa: F401
 from .mla_oracle import (  # noqa: F401
     absorb_q,
     attend_absorbed,

@@ -165,3 +165,49 @@ def test_cache_append_workspace_bytes():
     assert one % (576 * 4) == 0 and 1 <= one // (576 * 4) <= 7168 // 16
     # Many tokens: no split needed.
     assert lib.mla_cache_append_workspace_bytes(4096, 7168) == 4096 * 576 * 4
+
+
+def test_projection_argument_errors():
+    lib = _lib()
+    E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
+    ws = ctypes.c_void_p(0x100000)
+
+    def qp(**kw):
+        a = dict(x=FAKE, ws=ws, nbytes=1 << 40, M=4, d_model=7168, q_rank=1536, H=128, d_h=128,
+                 d_r=64, eps=1e-6, theta=10000.0)
+        a.update(kw)
+        return lib.mla_query_project(a["x"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["ws"],
+                                     a["nbytes"], a["M"], a["d_model"], a["q_rank"], a["H"],
+                                     a["d_h"], a["d_r"], ctypes.c_float(a["eps"]),
+                                     ctypes.c_float(a["theta"]), NULL)
+
+    assert qp(x=NULL) == E
+    assert qp(M=0) == E
+    assert qp(theta=-1.0) == E
+    assert qp(ws=ctypes.c_void_p(0x100008)) == E
+    assert qp(nbytes=8) == E
+    assert qp(H=64) == U
+    assert qp(q_rank=1000) == U
+    assert qp(d_model=7000) == U
+
+    def op(**kw):
+        a = dict(y=FAKE, ws=ws, nbytes=1 << 40, M=4, d_in=16384, d_out=7168)
+        a.update(kw)
+        return lib.mla_output_project(FAKE, FAKE, a["y"], a["ws"], a["nbytes"], a["M"],
+                                      a["d_in"], a["d_out"], NULL)
+
+    assert op(y=NULL) == E
+    assert op(y=ctypes.c_void_p(0x1002)) == E
+    assert op(M=-1) == E
+    assert op(nbytes=8) == E
+    assert op(d_in=100) == U
+    assert op(d_out=7000) == U
+
+
+def test_projection_workspace_bytes():
+    lib = _lib()
+    assert lib.mla_query_project_workspace_bytes(0, 7168, 1536) == 0
+    assert lib.mla_query_project_workspace_bytes(4, 7168, 1000) == 0
+    assert lib.mla_query_project_workspace_bytes(64, 7168, 1536) >= 64 * 128 * 192 * 4
+    assert lib.mla_output_project_workspace_bytes(4, 100, 7168) == 0
+    assert lib.mla_output_project_workspace_bytes(4096, 16384, 7168) == 4096 * 7168 * 4

@@ -107,3 +107,52 @@ def test_cache_append_placement():
                 assert np.all(np.isnan(out[blk, r]))
     # The input cache is left as it was.
     assert np.all(np.isnan(kv))
+
+
+# --- projections around the attention ----------------------------------------
+
+from oracle import projections as pj  # noqa: E402
+
+
+def test_query_project_hand_case():
+    # d_model 2, q_rank 2, one head with d_h = 1 and d_r = 2 (outputs: [q_C | q_R0, q_R1]).
+    x = np.array([[3.0, 4.0]])
+    w_dq = np.eye(2)                                   # c_q = (3, 4), RMS = sqrt(12.5)
+    gamma = np.array([1.0, 2.0])                       # c_q' = (3, 8) / sqrt(12.5)
+    w_uq = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    s = math.sqrt(12.5)
+    q_c, q_r = pj.query_project(x, w_dq, gamma, w_uq, positions=[1], eps=0.0, theta=10000.0,
+                                n_heads=1, d_h=1, d_r=2)
+    assert q_c[0, 0, 0] == pytest.approx(3 / s, rel=1e-15)
+    # Rotary pair (8/s, 11/s) turned by 1 radian (d_r = 2: inv_freq = 1).
+    a, b = 8 / s, 11 / s
+    np.testing.assert_allclose(q_r[0, 0], [a * math.cos(1) - b * math.sin(1),
+                                           a * math.sin(1) + b * math.cos(1)], rtol=1e-14)
+
+
+def test_query_project_structure():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 32))
+    w_dq = rng.standard_normal((16, 32))
+    gamma = 1 + 0.1 * rng.standard_normal(16)
+    w_uq = rng.standard_normal((4 * (8 + 4), 16))
+    args = dict(eps=1e-6, theta=10000.0, n_heads=4, d_h=8, d_r=4)
+    qc0, qr0 = pj.query_project(x, w_dq, gamma, w_uq, positions=[0, 0, 0], **args)
+    qc1, qr1 = pj.query_project(x, w_dq, gamma, w_uq, positions=[5, 900, 77777], **args)
+    np.testing.assert_array_equal(qc0, qc1)             # the content query has no position
+    # Position 0: the rotary query is the raw product's last 4 outputs of each head.
+    cq = ca.rms_norm(x @ w_dq.T, gamma, 1e-6)
+    raw = (cq @ w_uq.T).reshape(3, 4, 12)
+    np.testing.assert_allclose(qr0, raw[..., 8:], rtol=1e-13)
+    np.testing.assert_allclose(qc0, raw[..., :8], rtol=1e-13)
+    np.testing.assert_allclose(qr1[1], ca.apply_rope(raw[1, :, 8:], 900, 10000.0), rtol=1e-12)
+
+
+def test_output_project_against_brute_force():
+    rng = np.random.default_rng(7)
+    o = rng.standard_normal((2, 6))
+    w_o = rng.standard_normal((3, 6))
+    got = pj.output_project(o, w_o)
+    for m in range(2):
+        for d in range(3):
+            assert got[m, d] == pytest.approx(sum(o[m, j] * w_o[d, j] for j in range(6)), rel=1e-13)
