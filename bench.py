@@ -195,6 +195,53 @@ def bench_append(steps, warmup):
     return res
 
 
+def bench_projections(steps, warmup):
+    """Query projection (W_DQ, RMSNorm, W_UQ, RoPE) and output projection (W_O)
+    for the 64 tokens of one decode step: weight-streaming, HBM-bound."""
+    import torch
+    from mla_latent_kv_19_amd import api, synth
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    m = 64
+    x, w_dq, g, w_uq, pos = synth.query_inputs(m, seed=2700)
+    x, w_dq, g, w_uq = dev(x), dev(w_dq), dev(g), dev(w_uq)
+    pos = torch.from_numpy(pos).cuda()
+    q_c = torch.empty((m, 128, 128), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.empty((m, 128, 64), dtype=torch.bfloat16, device="cuda")
+    ws_q = torch.empty(api.load().mla_query_project_workspace_bytes(m, 7168, 1536),
+                       dtype=torch.uint8, device="cuda")
+    ms_q = timed(lambda: api.query_project(x, w_dq, g, w_uq, pos, q_c=q_c, q_r=q_r, workspace=ws_q))
+    bytes_q = (1536 * 7168 + 128 * 192 * 1536 + m * 7168 + m * 128 * 192) * 2
+    o, w_o = synth.output_inputs(m, seed=2701)
+    o, w_o = dev(o), dev(w_o)
+    y = torch.empty((m, 7168), dtype=torch.bfloat16, device="cuda")
+    ws_o = torch.empty(api.load().mla_output_project_workspace_bytes(m, 16384, 7168),
+                       dtype=torch.uint8, device="cuda")
+    ms_o = timed(lambda: api.output_project(o, w_o, y=y, workspace=ws_o))
+    bytes_o = (7168 * 16384 + m * 16384 + m * 7168) * 2
+    out = {}
+    for name, ms, b in (("query_project_64", ms_q, bytes_q), ("output_project_64", ms_o, bytes_o)):
+        gbs = b / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "gbs": gbs, "bound": "hbm", "frac": gbs / HBM_PEAK_GBS,
+                     "algorithmic_bytes": b}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -334,6 +381,7 @@ def main():
     }
     res["prefill"] = bench_prefill(max(3, args.steps // 4), 2)
     res["cache_append"] = bench_append(max(5, args.steps // 2), 3)
+    res["projections"] = bench_projections(max(5, args.steps // 2), 3)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, meta, args.cpu_seconds)
     else:
