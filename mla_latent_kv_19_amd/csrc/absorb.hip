@@ -29,6 +29,18 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* _
   const int l32 = lane & 31;
   const int wave = tid >> 6;
 
+  // Query operands of a block of 32 rows (lane: row m0 + l32, 8 consecutive i).
+  auto load_q = [&](int m0, bf16x8 (&bq)[8]) {
+    const int m = m0 + l32;
+    const uint16_t* src = q_c + ((size_t)min(m, M - 1) * 128 + h) * 128 + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = ld_global_bf16x8(src + 16 * ks);
+  };
+  // The first block's queries are loaded before the weight slice is staged, so
+  // the two loads overlap.
+  bf16x8 bq[8];
+  load_q(0, bq);
+
   // Stage W_UK[h][0:128][128*jblk : +128]: 128 rows x 256 B = 2048 16-byte chunks.
   const uint16_t* wsrc = w_uk + (size_t)h * 128 * 512 + jblk * 128;
 #pragma unroll
@@ -56,20 +68,14 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* _
   }
 
   for (int m0 = 0; m0 < M; m0 += 32) {
-    const int m = m0 + l32;
-    bf16x8 bq[8];
-    if (m < M) {
-      const uint16_t* src = q_c + ((size_t)m * 128 + h) * 128 + 8 * half;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bq[ks] = ld_global_bf16x8(src + 16 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bq[ks] = bf16x8{};
-    }
+    // Next block's queries in flight during this block's product.
+    bf16x8 bn[8];
+    if (m0 + 32 < M) load_q(m0 + 32, bn);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
     // acc[r]: j = 32*wave + 8*(r/4) + 4*half + r%4, m = m0 + l32.
+    const int m = m0 + l32;
     if (m < M) {
       uint16_t* dst = q_lat + ((size_t)m * 128 + h) * 512 + jblk * 128 + 32 * wave + 4 * half;
 #pragma unroll
@@ -80,6 +86,8 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* _
         *reinterpret_cast<bf16x4*>(dst + 8 * g) = v;
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = bn[ks];
   }
 }
 

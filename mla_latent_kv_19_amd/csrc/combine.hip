@@ -40,6 +40,31 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   const int wave = tid >> 6;
   const size_t split_stride = (size_t)M * 128;   // rows of one split
 
+  // W_UV[h] rows 128jc .. 128jc+127 (128 x 16 sixteen-byte chunks), staged
+  // through registers: the loads of slice 0 are issued first, to overlap the
+  // split merge below, and each next slice's during the current one's product.
+  const uint16_t* wsrc = w_uv + (size_t)h * 512 * 128;
+  uint4 wr0, wr1, wr2, wr3, wr4, wr5, wr6, wr7;
+#define MLA_CMB_W_SRC(k, jc) \
+  (*reinterpret_cast<const uint4*>(wsrc + (size_t)((jc) * 128 + (((k) * kCmbThreads + tid) >> 4)) * 128 + \
+                                   (((k) * kCmbThreads + tid) & 15) * 8))
+#define MLA_CMB_W_DST(k) \
+  (*reinterpret_cast<uint4*>(&wt[(((k) * kCmbThreads + tid) >> 4) * kWPitch + (((k) * kCmbThreads + tid) & 15) * 8]))
+#define MLA_CMB_LOAD_W(jc)                                                   \
+  do {                                                                       \
+    wr0 = MLA_CMB_W_SRC(0, jc); wr1 = MLA_CMB_W_SRC(1, jc);                  \
+    wr2 = MLA_CMB_W_SRC(2, jc); wr3 = MLA_CMB_W_SRC(3, jc);                  \
+    wr4 = MLA_CMB_W_SRC(4, jc); wr5 = MLA_CMB_W_SRC(5, jc);                  \
+    wr6 = MLA_CMB_W_SRC(6, jc); wr7 = MLA_CMB_W_SRC(7, jc);                  \
+  } while (0)
+#define MLA_CMB_STORE_W()                                                    \
+  do {                                                                       \
+    MLA_CMB_W_DST(0) = wr0; MLA_CMB_W_DST(1) = wr1; MLA_CMB_W_DST(2) = wr2;  \
+    MLA_CMB_W_DST(3) = wr3; MLA_CMB_W_DST(4) = wr4; MLA_CMB_W_DST(5) = wr5;  \
+    MLA_CMB_W_DST(6) = wr6; MLA_CMB_W_DST(7) = wr7;                          \
+  } while (0)
+  MLA_CMB_LOAD_W(0);
+
   // 1. Split weights per row.
   if (tid < 32) {
     const int m = m0 + tid;
@@ -60,31 +85,45 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   }
   __syncthreads();
 
-  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2k.
+  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2k,
+  // four rows at a time (the partials of four rows and up to four splits in
+  // flight together).
   {
     const int cq = tid & 127;
-    for (int r = tid >> 7; r < 32; r += 2) {
-      const int m = m0 + r;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m < M) {
-        const float* src = part_o + ((size_t)m * 128 + h) * 512 + 4 * cq;
-        for (int s = 0; s < S; ++s) {
-          const float w = wts[s * 32 + r];
-          if (w != 0.f) {
-            const float4 v = *reinterpret_cast<const float4*>(src + s * split_stride * 512);
-            o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
+    for (int r0 = tid >> 7; r0 < 32; r0 += 8) {
+      float4 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+      for (int s = 0; s < S; ++s) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int m = min(m0 + r0 + 2 * u, M - 1);
+          v[u] = *reinterpret_cast<const float4*>(part_o + (s * split_stride + (size_t)m * 128 + h) * 512 +
+                                                  4 * cq);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = (m0 + r0 + 2 * u < M) ? wts[s * 32 + r0 + 2 * u] : 0.f;
+          if (w != 0.f) {          // an empty split may hold -inf/NaN-free zeros; skip it anyway
+            o[u].x += w * v[u].x; o[u].y += w * v[u].y; o[u].z += w * v[u].z; o[u].w += w * v[u].w;
           }
         }
       }
-      const float ov[4] = {o.x, o.y, o.z, o.w};
-      bf16x4 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)ov[e];
-        lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + 2 * u;
+        const float ov[4] = {o[u].x, o[u].y, o[u].z, o[u].w};
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (__bf16)ov[e];
+          lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+        }
+        *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
+        *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
       }
-      *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
-      *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
     }
   }
 
@@ -96,17 +135,12 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   const lds_u8* ahb = to_lds(o_hi) + (l32 * kOPitch + 8 * half) * 2;
   const lds_u8* alb = to_lds(o_lo) + (l32 * kOPitch + 8 * half) * 2;
   f32x16 acc = {};
-  const uint16_t* wsrc = w_uv + (size_t)h * 512 * 128;
-  for (int jc = 0; jc < 4; ++jc) {
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int chunk = k * kCmbThreads + tid;   // 128 rows x 16 chunks
-      const int j = chunk >> 4, c = chunk & 15;
-      *reinterpret_cast<uint4*>(&wt[j * kWPitch + c * 8]) =
-          *reinterpret_cast<const uint4*>(wsrc + (size_t)(jc * 128 + j) * 128 + c * 8);
-    }
+  for (int jc = 0; jc < 4; ++jc) {
+    __syncthreads();                 // every wave is done with the previous slice
+    MLA_CMB_STORE_W();
     __syncthreads();
+    if (jc + 1 < 4) MLA_CMB_LOAD_W(jc + 1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x4 blo = ld_lds_tr(trb + (16 * ks) * kWPitch * 2);
@@ -117,6 +151,10 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
       acc = mfma32(ld_lds_bf16x8(alb + koff), bw, acc);
     }
   }
+#undef MLA_CMB_W_SRC
+#undef MLA_CMB_W_DST
+#undef MLA_CMB_LOAD_W
+#undef MLA_CMB_STORE_W
   // acc[r]: row m0 + 8*(r/4) + 4*half + r%4, column 32*wave + l32.
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
