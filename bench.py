@@ -317,6 +317,38 @@ def main():
     ms_step = float(step_ms.mean())
     del flush
 
+    # The same step captured once in a HIP graph and replayed: one launch per
+    # step instead of three host calls, so the host cannot leave the GPU idle
+    # between kernels.  Same flush before each replay, outside the events.
+    graph_ms = None
+    try:
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            graph.replay()
+        gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(gevs):
+            flush.fill_(i & 255)
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        graph_ms = np.array([a.elapsed_time(b) for a, b in gevs])
+        del flush, graph
+    except RuntimeError as exc:          # capture unsupported: report eager only
+        print(f"graph capture skipped: {exc}", file=sys.stderr)
+
     # Per-kernel launch durations, events on the stream the kernels run on.
     def time_kernel(fn, n):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -352,6 +384,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "ms_step_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "ms_per_step_graph": None if graph_ms is None else float(graph_ms.mean()),
+        "ms_step_graph_p10_p50_p90": None if graph_ms is None else
+        [float(np.percentile(graph_ms, q)) for q in (10, 50, 90)],
         "flush_between_steps_bytes": FLUSH_BYTES,
         "higher_is_better": True,
         "scaling": "weak",
