@@ -45,7 +45,22 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
   float v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  // K slices four at a time, so that up to 64 loads per thread are in flight.
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {
+    float t[4][16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* p = part + ((size_t)(s + u) * M + m) * N + tid;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) t[u][j] = (j < per) ? p[256 * j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] += t[u][j];
+  }
+  for (; s < splits; ++s) {
     const float* p = part + ((size_t)s * M + m) * N + tid;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
