@@ -11,14 +11,17 @@
 // values once and runs a flash-attention kernel over them:
 //
 //   prefill_kv_kernel   K_C[b,h,t,:] = W_UK[h] c_t          (bf16, [B,H,Lpad,128])
-//                       V^T[b,h,:,t] = (c_t W_UV[h])^T      (bf16, [B,H,128,Lpad],
-//                                                             keys permuted in 16s)
+//                       V^T[b,h,:,t] = (c_t W_UV[h])^T      (bf16, tile-major
+//                                        [B,H,Lpad/64,128,64], keys permuted in 16s)
 //   prefill_attn_kernel out[b,i,h,:] = softmax(q . k * scale, causal) V
 //
 // Work decomposition (MI355X):
 //   * reconstruction: one work-group per (sequence, head, 128 positions); the
-//     128x512 latent block is the A operand read straight from the paged
-//     cache, W_UK[h] and W_UV[h] are staged through LDS in 64-row slices;
+//     128x512 latent block is an MFMA operand read straight from the paged
+//     cache, W_UK[h] and W_UV[h] are staged through LDS in 64-row slices; the
+//     outputs leave through LDS as whole 16-byte chunks of contiguous rows
+//     (a 128-position block of K_C and two 64-key V^T tiles are each one
+//     contiguous 32 KB range);
 //   * attention: one work-group of 8 waves (2 per SIMD) per (sequence, head,
 //     256 queries), wave w owning 32 queries; 64-key tiles ([K_C | k_R] and
 //     V^T) stream into LDS with direct-to-LDS loads through a 3-stage ring; S^T = K Q^T and
@@ -85,8 +88,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
 
   const uint16_t* wuk = w_uk + (size_t)h * 128 * 512;
   const uint16_t* wuv = w_uv + (size_t)h * 512 * 128;
-  // B operand for K_C (W_UK^T: k = j, n = i): lane reads row i = 32n + l32,
-  // 8 consecutive j at 16*ks + 8*half.
+  // W_UK as the A operand of K_C^T (rows i, k = j): lane reads row i = 32n + l32,
+  // 8 consecutive j at 16*ks + 8*half.  The latent block is then the B operand
+  // (columns = positions), so each lane ends up holding 4 consecutive dims of
+  // one position, as it does for V^T.
   const int wk_rd = (l32 * kWkPitch + 8 * half) * 2;
   // B operand for V (W_UV: k = j, n = d) by transposed reads: group g = lane/16
   // supplies rows j = 16*ks + 8*(g/2) + q/4 (+4), columns 32n + 16*(g%2) + 4*(q%4).
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const bf16x8 bk = ld_lds_bf16x8(wk_l + (32 * n * kWkPitch + 16 * ks) * 2);
-        acc_k[n] = mfma32(a[ks], bk, acc_k[n]);
+        acc_k[n] = mfma32(bk, a[ks], acc_k[n]);
         const bf16x4 lo = ld_lds_tr(wv_l + ((16 * ks) * kWvPitch + 32 * n) * 2);
         const bf16x4 hi = ld_lds_tr(wv_l + ((16 * ks + 4) * kWvPitch + 32 * n) * 2);
         acc_v[n] = mfma32(a[ks], cat(lo, hi), acc_v[n]);
@@ -171,28 +176,69 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
 #undef MLA_PF_LOAD_SLICE
 #undef MLA_PF_STORE_SLICE
 
-  // acc[n][r]: token t0 + 32*wave + 8*(r/4) + 4*half + r%4, column 32n + l32.
-  uint16_t* kdst = ws_k + ((size_t)(b * 128 + h) * Lpad) * 128;
-  uint16_t* vdst = ws_vt + ((size_t)(b * 128 + h) * 128) * Lpad;
+  // acc_k[n][r]: dim 32n + 8*(r/4) + 4*half + r%4 of position t0 + 32*wave + l32;
+  // acc_v[n][r]: dim 32n + l32 of position t0 + 32*wave + 8*(r/4) + 4*half + r%4.
+  // Positions at or past L are written as zeros.  Both go to LDS as 8-byte
+  // pieces (the weight buffers are free once every wave is past this barrier):
+  //   K block  [128 positions][16 chunks of 8 dims], chunk c at c ^ (pos & 15);
+  //   V^T      [2 tiles][128 dims][8 chunks of 8 keys], chunk c at c ^ ((d >> 1) & 7),
+  //            keys in vt_pos() order inside each 16-key group.
+  __syncthreads();
+  lds_u8* kst = to_lds(wk);                    // 32 KB of the 36 KB W_UK buffers
+  lds_u8* vst = to_lds(wv);                    // 32 KB of the 38 KB W_UV buffers
+  {
+    const int pk = 32 * wave + l32;            // this lane's K position in the block
+    const bool k_ok = t0 + pk < L;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int tb = t0 + 32 * wave + 8 * g + 4 * half;   // first of 4 consecutive tokens
-    if (tb >= Lpad) continue;                           // the last 128-block may overhang
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int col = 32 * n + l32;
-      bf16x4 vv;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 kk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = tb + e;
-        const bool ok = t < L;
-        const __bf16 kvl = (__bf16)(ok ? acc_k[n][4 * g + e] : 0.f);
-        kdst[(size_t)t * 128 + col] = __builtin_bit_cast(uint16_t, kvl);
-        vv[e] = (__bf16)(ok ? acc_v[n][4 * g + e] : 0.f);
+        for (int e = 0; e < 4; ++e) kk[e] = (__bf16)(k_ok ? acc_k[n][4 * g + e] : 0.f);
+        const int c = (4 * n + g) ^ (pk & 15);
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(kst + pk * 256 + c * 16 +
+                                                                     half * 8) = kk;
       }
-      // Four consecutive tokens stay contiguous under vt_pos().
-      *reinterpret_cast<bf16x4*>(vdst + (size_t)col * Lpad + vt_pos(tb)) = vv;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int pv = 32 * wave + 8 * g + 4 * half;      // first of 4 consecutive positions
+      const int u = vt_pos(pv & 63);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int d = 32 * n + l32;
+        bf16x4 vv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = (__bf16)(t0 + pv + e < L ? acc_v[n][4 * g + e] : 0.f);
+        const int c = (u >> 3) ^ ((d >> 1) & 7);
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(
+            vst + (pv >> 6) * 16384 + d * 128 + c * 16 + (u & 7) * 2) = vv;
+      }
     }
+  }
+  __syncthreads();
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // 2048 chunks of each output per work-group, 8 per thread.  Positions past
+  // Lpad (the last 128-block may overhang by one 64-key tile) are not stored.
+  uint16_t* kdst = ws_k + ((size_t)(b * 128 + h) * Lpad + t0) * 128;
+  uint16_t* vdst = ws_vt + ((size_t)(b * 128 + h) * Lpad + t0) * 128;   // tile t0 / 64
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = k * kPfThreads + tid;
+    const int r = q >> 4, c = q & 15;
+    if (t0 + r < Lpad)
+      *reinterpret_cast<u32x4*>(kdst + r * 128 + c * 8) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(kst + r * 256 +
+                                                                             (c ^ (r & 15)) * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int q = k * kPfThreads + tid;
+    const int tile = q >> 10, d = (q >> 3) & 127, c = q & 7;
+    if (t0 + 64 * tile < Lpad)
+      *reinterpret_cast<u32x4*>(vdst + (tile * 128 + d) * 64 + c * 8) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+              vst + tile * 16384 + d * 128 + (c ^ ((d >> 1) & 7)) * 16);
   }
 }
 
@@ -231,8 +277,8 @@ __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 // otherwise schedules.
 __device__ __forceinline__ void issue_kv_tile(const uint16_t* kc_src,   // ws_k row of key k0
                                               const uint16_t* kr_page,  // cache block of keys k0..
-                                              const uint16_t* vt_src,   // ws_vt + k0 (row d = 0)
-                                              int Lpad, lds_u8* stage, int tid) {
+                                              const uint16_t* vt_src,   // V^T tile of keys k0..
+                                              lds_u8* stage, int tid) {
   lds_u8* kdst = stage + (tid & ~63) * 16;
 #pragma unroll
   for (int it = 0; it < kKSlotsPerThread; ++it) {
@@ -250,7 +296,7 @@ __device__ __forceinline__ void issue_kv_tile(const uint16_t* kc_src,   // ws_k 
     const int slot = it * kAttnThreads + tid;
     const int d = slot >> 3;
     const int c = (slot & 7) ^ v_swz(d);
-    g2lds16(vt_src + (size_t)d * Lpad + c * 8, vdst + it * kAttnThreads * 16);
+    g2lds16(vt_src + d * 64 + c * 8, vdst + it * kAttnThreads * 16);
   }
 }
 
@@ -303,13 +349,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
   }
 
   const uint16_t* kc_base = ws_k + ((size_t)(b * 128 + h) * Lpad) * 128;
-  const uint16_t* vt_base = ws_vt + ((size_t)(b * 128 + h) * 128) * Lpad;
+  const uint16_t* vt_base = ws_vt + ((size_t)(b * 128 + h) * 128) * Lpad;   // 64-key tiles of 8192
   const int32_t* table = block_table + (size_t)b * max_blocks;
 
   auto issue = [&](int tile, lds_u8* stage) {
     const int k0 = tile * kKeyTile;
-    issue_kv_tile(kc_base + (size_t)k0 * 128, kv + (size_t)table[k0 >> 6] * 64 * 576, vt_base + k0,
-                  Lpad, stage, tid);
+    issue_kv_tile(kc_base + (size_t)k0 * 128, kv + (size_t)table[k0 >> 6] * 64 * 576, vt_base + (size_t)k0 * 128,
+                  stage, tid);
   };
   issue(0, smem);
   if (n_tiles > 1) issue(1, smem + kStageBytes);
