@@ -6,11 +6,19 @@
 //   part[s, m, n] = sum over k in K slice s of x[m, k] * w[n, k]
 //
 // x is [M, K] and w is a linear layer's [N, K] weight, both bf16 and
-// k-contiguous, so every MFMA 32x32x16 operand is one 16-byte load per lane
-// straight from global memory: one wave per (64 rows, 64 outputs, K slice),
-// four k-steps of loads in flight.  The K split is chosen so that about 512
-// waves cover the chip even for a single decode batch, which streams each
-// weight once at HBM rate; the callers' finish kernels sum the slices.
+// k-contiguous.  Two kernels, one output contract (the callers' finish
+// kernels sum the slices):
+//  * linear_stream_kernel, M <= 64 (a decode batch), K a multiple of 64: the
+//    weight is the traffic.  A work-group of 4 waves takes 256 outputs and a
+//    K slice; chunks of 64 k of the weight rows (256 x 128 B) and of x
+//    (64 x 128 B) stream into a 3-stage LDS ring with direct-to-LDS loads, each
+//    load instruction covering 8 rows x 128 contiguous bytes, and the MFMA
+//    operands are read from LDS (chunk swizzle: conflict-free).
+//  * linear_splitk_kernel otherwise: one wave per (64 rows, 64 outputs, K
+//    slice), every MFMA 32x32x16 operand one 16-byte load per lane straight
+//    from global memory, four k-steps of loads in flight.
+// The K split is chosen so that a few hundred work-groups cover the chip even
+// for a single decode batch.
 #include "mla_common.h"
 
 namespace mla {
@@ -85,11 +93,142 @@ __global__ __launch_bounds__(64) void linear_splitk_kernel(const uint16_t* __res
     }
 }
 
+constexpr int kLsThreads = 256;                          // 4 waves
+constexpr int kLsN = 256;                                // outputs per work-group
+constexpr int kLsKc = 64;                                // k per chunk
+constexpr int kLsStages = 3;
+constexpr int kLsWBytes = kLsN * kLsKc * 2;              // 32768
+constexpr int kLsXBytes = 64 * kLsKc * 2;                // 8192
+constexpr int kLsStageBytes = kLsWBytes + kLsXBytes;     // 40960
+constexpr int kLsWLoads = kLsWBytes / 16 / kLsThreads;   // 8 per thread per chunk
+constexpr int kLsXLoads = kLsXBytes / 16 / kLsThreads;   // 2
+constexpr int kLsLoads = kLsWLoads + kLsXLoads;          // 10
+static_assert(kLsWLoads * 16 * kLsThreads == kLsWBytes && kLsXLoads * 16 * kLsThreads == kLsXBytes,
+              "chunk split");
+
+// A chunk row is 8 sixteen-byte pieces (128 B); piece c of row r sits at
+// position c ^ ((r >> 1) & 7), so the 16 rows that a 16-lane group of an
+// operand read touches fall on 16 distinct 4-bank groups.
+__device__ __forceinline__ int ls_swz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(kLsThreads, 1) void linear_stream_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ part,
+    int M, int N, int K, int chunks_per_split) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char ls_smem[];
+  lds_u8* smem = to_lds(ls_smem);
+  const int n_tiles = (N + kLsN - 1) / kLsN;
+  const int n0 = (blockIdx.x % n_tiles) * kLsN;
+  const int split = blockIdx.x / n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = split * chunks_per_split;
+  const int nch = min(K / kLsKc, c0 + chunks_per_split) - c0;
+
+  // Load sources, fixed but for the chunk's k offset: slot = it * 256 + tid
+  // fills LDS bytes [16 slot, 16 slot + 16) of its region: row slot / 8,
+  // position slot % 8, which holds piece (slot % 8) ^ ls_swz(row).  Rows past
+  // N or M read a valid row (their results are never stored).
+  const uint16_t* wsrc[kLsWLoads];
+  const uint16_t* xsrc[kLsXLoads];
+#pragma unroll
+  for (int it = 0; it < kLsWLoads; ++it) {
+    const int slot = it * kLsThreads + tid, r = slot >> 3;
+    wsrc[it] = w + (size_t)min(n0 + r, N - 1) * K + (((slot & 7) ^ ls_swz(r)) * 8) + (size_t)c0 * kLsKc;
+  }
+#pragma unroll
+  for (int it = 0; it < kLsXLoads; ++it) {
+    const int slot = it * kLsThreads + tid, r = slot >> 3;
+    xsrc[it] = x + (size_t)min(r, M - 1) * K + (((slot & 7) ^ ls_swz(r)) * 8) + (size_t)c0 * kLsKc;
+  }
+  auto issue = [&](int ci) {
+    lds_u8* st = smem + (ci % kLsStages) * kLsStageBytes + (tid & ~63) * 16;
+#pragma unroll
+    for (int it = 0; it < kLsWLoads; ++it)
+      g2lds16_opaque(wsrc[it] + ci * kLsKc, st + it * kLsThreads * 16);
+#pragma unroll
+    for (int it = 0; it < kLsXLoads; ++it)
+      g2lds16_opaque(xsrc[it] + ci * kLsKc, st + kLsWBytes + it * kLsThreads * 16);
+  };
+
+  // Operand reads: x rows 32a + l32 (A), weight rows 64 wave + 32t + l32 (B);
+  // k-step ks of a chunk is piece 2ks + half of the row.
+  int xoff[2], woff[2], xsw[2], wsw[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int xr = 32 * t + l32, wr = 64 * wave + 32 * t + l32;
+    xoff[t] = kLsWBytes + xr * 128;
+    woff[t] = wr * 128;
+    xsw[t] = ls_swz(xr);
+    wsw[t] = ls_swz(wr);
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  issue(0);
+  if (nch > 1) issue(1);
+  for (int ci = 0; ci < nch; ++ci) {
+    // Chunk ci has landed for every thread; every wave is done with chunk
+    // ci-1, whose stage then takes chunk ci+2.
+    if (ci + 1 < nch) wait_vmcnt<kLsLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if (ci + 2 < nch) issue(ci + 2);
+    const lds_u8* st = smem + (ci % kLsStages) * kLsStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int pc = 2 * ks + half;
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        av[t] = ld_lds_bf16x8(st + xoff[t] + ((pc ^ xsw[t]) * 16));
+        bv[t] = ld_lds_bf16x8(st + woff[t] + ((pc ^ wsw[t]) * 16));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(av[a], bv[b], acc[a][b]);
+    }
+  }
+
+  // acc[a][b][r]: row 32a + 8(r/4) + 4*half + r%4, output n0 + 64 wave + 32b + l32.
+  float* dst = part + (size_t)split * M * N;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int n = n0 + 64 * wave + 32 * b + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * a + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < M) dst[(size_t)m * N + n] = acc[a][b][r];
+      }
+  }
+}
+
 }  // namespace mla
 
-// K slices for an [M, K] x [N, K]^T product: about 512 waves in total, at
-// least one k-step (16 values) per slice.  N must be a multiple of 64.
+// Whether the streaming kernel takes an [M, K] x [N, K]^T product.
+static bool use_stream(int M, int N, int K) {
+  return M >= 1 && M <= 64 && K % mla::kLsKc == 0 && N % 64 == 0;
+}
+
+// K slices for an [M, K] x [N, K]^T product.  Streaming kernel: about 384
+// work-groups, at least 4 chunks (256 k) per slice.  Split-K kernel: about
+// 512 waves, at least one k-step (16 values) per slice.  N must be a multiple
+// of 64.
 extern "C" int mla_linear_splits(int M, int N, int K) {
+  if (use_stream(M, N, K)) {
+    const int tiles = (N + mla::kLsN - 1) / mla::kLsN;
+    const int chunks = K / mla::kLsKc;
+    int s = (384 + tiles - 1) / tiles;
+    const int smax = (chunks + 3) / 4;
+    s = s < 1 ? 1 : (s > smax ? smax : s);
+    const int per = (chunks + s - 1) / s;
+    return (chunks + per - 1) / per;
+  }
   const int tiles = ((M + 63) / 64) * (N / 64);
   const int ksteps = K / 16;
   int s = (512 + tiles - 1) / tiles;
@@ -101,6 +240,19 @@ extern "C" int mla_linear_splits(int M, int N, int K) {
 extern "C" hipError_t mla_launch_linear_splitk(const uint16_t* x, const uint16_t* w, float* part,
                                                int M, int N, int K, int splits,
                                                hipStream_t stream) {
+  if (use_stream(M, N, K)) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&mla::linear_stream_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, mla::kLsStages * mla::kLsStageBytes);
+    if (attr != hipSuccess) return attr;
+    const int chunks = K / mla::kLsKc;
+    int per = (chunks + splits - 1) / splits;
+    void* args[] = {&x, &w, &part, &M, &N, &K, &per};
+    const int n_tiles = (N + mla::kLsN - 1) / mla::kLsN;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&mla::linear_stream_kernel),
+                           dim3(n_tiles * splits), dim3(mla::kLsThreads), args,
+                           mla::kLsStages * mla::kLsStageBytes, stream);
+  }
   const int ksteps = K / 16;
   int per = (ksteps + splits - 1) / splits;
   void* args[] = {&x, &w, &part, &M, &N, &K, &per};
