@@ -7,7 +7,7 @@ the query), split-KV attention over the paged latent cache, log-sum-exp
 combine and the W_UV up-projection.  Inputs are seeded synthetic data with
 the shapes of the pages' model (128 heads, latent 512 + rotary 64, content
 head 128) and are resident in HBM before timing starts.  Each timed step is
-bracketed by its own HIP events; a 512 MiB write before each step (outside
+bracketed by its own HIP events; a 512 MiB read before each step (outside
 the events) leaves no cache state from the previous step.  ms_per_step is the
 mean over the timed steps, with p10 / p50 / p90 alongside.
 
@@ -36,6 +36,22 @@ ROW_BYTES = 576 * 2            # one cached token: latent 512 + rotary key 64, b
 FLOP_PER_TOKEN_QUERY = 128 * 2 * (576 + 512)   # scores + value product, all heads
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_headline_traffic.json")
 FLUSH_BYTES = 512 << 20
+
+
+class _Flush:
+    """Evicts the 4 MB L2s and the 256 MB Infinity Cache before a timed call by
+    reading 512 MiB (a sum over a zero buffer).  A write would do it too, but
+    it leaves dirty lines whose write-back then competes with the timed
+    kernel's reads: measured here, a 235 MB read runs at 2.8 TB/s after a
+    512 MiB write and at 5.5 TB/s after a 512 MiB read."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = None
+
+    def __call__(self):
+        self.sink = self.buf.sum()
 
 
 def parse():
@@ -112,6 +128,27 @@ def cpu_baseline(wl, inp_meta, budget_s):
                       f"{tokens} KV tokens), un-absorbed fp64 numpy oracle, {spent:.1f} s"}
 
 
+def _timed_cold(fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls, each timed alone (HIP events on the
+    current stream) after a 512 MiB read that evicts L2 and the MALL, so the
+    weights a call streams come from HBM."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    flush = _Flush()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    del flush
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
 def bench_prefill(steps, warmup):
     """Causal prefill, T = L = 4096, B = 1 (reconstruction + attention), on MFMA."""
     import torch
@@ -134,16 +171,7 @@ def bench_prefill(steps, warmup):
     def run():
         api.prefill(q_c, q_r, kv, table, lens, w_uk, w_uv, wl.scale, out=out, workspace=ws)
 
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = _timed_cold(run, steps, warmup)
     pairs = T * (T + 1) // 2
     flops = pairs * 128 * 2 * (192 + 128) + T * 128 * 512 * 256 * 2
     tflops = flops / (ms * 1e-3) / 1e12
@@ -174,17 +202,7 @@ def bench_append(steps, warmup):
         def run():
             api.cache_append(x, w, g, seq, pos, table, kv, workspace=ws)
 
-        for _ in range(warmup):
-            run()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record()
-            run()
-            e1.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        ms = _timed_cold(run, steps, warmup)
         flop = 2.0 * m * 7168 * 576
         hbm = 576 * 7168 * 2 + m * 7168 * 2 + m * 576 * 2 + 512 * 2      # weight, x, rows, gain
         res[f"tokens_{m}"] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12,
@@ -205,17 +223,7 @@ def bench_projections(steps, warmup):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record()
-            fn()
-            e1.record()
-        torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        return _timed_cold(fn, steps, warmup)
 
     m = 64
     x, w_dq, g, w_uq, pos = synth.query_inputs(m, seed=2700)
@@ -299,15 +307,15 @@ def main():
     for _ in range(args.warmup):
         step()
     # Timed steps: HIP events around each step; before each, outside the events,
-    # a 512 MiB write evicts the 4 MB L2s and the 256 MB Infinity Cache, so no
+    # a 512 MiB read evicts the 4 MB L2s and the 256 MB Infinity Cache, so no
     # step finds the previous step's weights or queries on chip.
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = _Flush()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for i, (a, b) in enumerate(evs):
-        flush.fill_(i & 255)
+    for a, b in evs:
+        flush()
         a.record()
         step()
         b.record()
@@ -332,14 +340,14 @@ def main():
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        flush = _Flush()
         for _ in range(args.warmup):
             graph.replay()
         gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
         torch.cuda.synchronize()
-        for i, (a, b) in enumerate(gevs):
-            flush.fill_(i & 255)
+        for a, b in gevs:
+            flush()
             a.record()
             graph.replay()
             b.record()
@@ -349,11 +357,15 @@ def main():
     except RuntimeError as exc:          # capture unsupported: report eager only
         print(f"graph capture skipped: {exc}", file=sys.stderr)
 
-    # Per-kernel launch durations, events on the stream the kernels run on.
+    # Per-kernel launch durations, events on the stream the kernels run on,
+    # each launch after the same cache-evicting read as the steps.
+    kflush = _Flush()
+
     def time_kernel(fn, n):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
         for a, b in evs:
+            kflush()
             a.record()
             fn()
             b.record()
@@ -365,6 +377,7 @@ def main():
     t_decode = time_kernel(lambda: api.decode_paged(q_lat, q_r, kv, table, lens, wl.scale, splits,
                                                     part_o, part_lse), n_k)
     t_combine = time_kernel(lambda: api.combine(part_o, part_lse, w_uv, out=out), n_k)
+    del kflush
 
     kv_bytes = kv_tokens * ROW_BYTES
     weight_bytes = 2 * 128 * 128 * 512 * 2
