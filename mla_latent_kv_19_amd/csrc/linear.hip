@@ -14,6 +14,11 @@
 //    (64 x 128 B) stream into a 3-stage LDS ring with direct-to-LDS loads, each
 //    load instruction covering 8 rows x 128 contiguous bytes, and the MFMA
 //    operands are read from LDS (chunk swizzle: conflict-free).
+//  * linear_tile_kernel, M > 64 with N a multiple of 192 and K of 64 (a
+//    prefill chunk): MFMA-bound.  A work-group of 4 waves (2 x 2) takes a
+//    128 x 192 output tile and a K slice; 64-k chunks of the x and weight
+//    rows (16 + 24 KB) go through the same kind of 3-stage LDS ring, each wave
+//    computing 64 x 96 outputs (6 MFMA blocks per k-step from 5 operand reads).
 //  * linear_splitk_kernel otherwise: one wave per (64 rows, 64 outputs, K
 //    slice), every MFMA 32x32x16 operand one 16-byte load per lane straight
 //    from global memory, four k-steps of loads in flight.
@@ -208,18 +213,140 @@ __global__ __launch_bounds__(kLsThreads, 1) void linear_stream_kernel(
   }
 }
 
+
+constexpr int kLtBM = 128, kLtBN = 192;
+constexpr int kLtXBytes = kLtBM * kLsKc * 2;             // 16384
+constexpr int kLtWBytes = kLtBN * kLsKc * 2;             // 24576
+constexpr int kLtStageBytes = kLtXBytes + kLtWBytes;     // 40960
+constexpr int kLtXLoads = kLtXBytes / 16 / kLsThreads;   // 4 per thread per chunk
+constexpr int kLtWLoads = kLtWBytes / 16 / kLsThreads;   // 6
+constexpr int kLtLoads = kLtXLoads + kLtWLoads;          // 10
+static_assert(kLtXLoads * 16 * kLsThreads == kLtXBytes && kLtWLoads * 16 * kLsThreads == kLtWBytes,
+              "tile chunk split");
+
+__global__ __launch_bounds__(kLsThreads, 1) void linear_tile_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ part,
+    int M, int N, int K, int chunks_per_split) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lt_smem[];
+  lds_u8* smem = to_lds(lt_smem);
+  const int n_tiles = N / kLtBN, m_tiles = (M + kLtBM - 1) / kLtBM;
+  const int n0 = (blockIdx.x % n_tiles) * kLtBN;
+  const int m0 = ((blockIdx.x / n_tiles) % m_tiles) * kLtBM;
+  const int split = blockIdx.x / (n_tiles * m_tiles);
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;       // rows 64 wm.., outputs 96 wn..
+  const int c0 = split * chunks_per_split;
+  const int nch = min(K / kLsKc, c0 + chunks_per_split) - c0;
+
+  // Load sources as in linear_stream_kernel (rows past M read a valid row;
+  // their results are never stored).
+  const uint16_t* xsrc[kLtXLoads];
+  const uint16_t* wsrc[kLtWLoads];
+#pragma unroll
+  for (int it = 0; it < kLtXLoads; ++it) {
+    const int slot = it * kLsThreads + tid, r = slot >> 3;
+    xsrc[it] = x + (size_t)min(m0 + r, M - 1) * K + (((slot & 7) ^ ls_swz(r)) * 8) + (size_t)c0 * kLsKc;
+  }
+#pragma unroll
+  for (int it = 0; it < kLtWLoads; ++it) {
+    const int slot = it * kLsThreads + tid, r = slot >> 3;
+    wsrc[it] = w + (size_t)(n0 + r) * K + (((slot & 7) ^ ls_swz(r)) * 8) + (size_t)c0 * kLsKc;
+  }
+  auto issue = [&](int ci) {
+    lds_u8* st = smem + (ci % kLsStages) * kLtStageBytes + (tid & ~63) * 16;
+#pragma unroll
+    for (int it = 0; it < kLtXLoads; ++it)
+      g2lds16_opaque(xsrc[it] + ci * kLsKc, st + it * kLsThreads * 16);
+#pragma unroll
+    for (int it = 0; it < kLtWLoads; ++it)
+      g2lds16_opaque(wsrc[it] + ci * kLsKc, st + kLtXBytes + it * kLsThreads * 16);
+  };
+
+  // Operand reads: x rows 64 wm + 32a + l32 (A), weight rows 96 wn + 32b + l32 (B).
+  int xoff[2], xsw[2], woff[3], wsw[3];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int r = 64 * wm + 32 * a + l32;
+    xoff[a] = r * 128;
+    xsw[a] = ls_swz(r);
+  }
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const int r = 96 * wn + 32 * b + l32;
+    woff[b] = kLtXBytes + r * 128;
+    wsw[b] = ls_swz(r);
+  }
+  f32x16 acc[2][3];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) acc[a][b] = f32x16{};
+
+  issue(0);
+  if (nch > 1) issue(1);
+  for (int ci = 0; ci < nch; ++ci) {
+    // Chunk ci has landed for every thread; every wave is done with chunk
+    // ci-1, whose stage then takes chunk ci+2.
+    if (ci + 1 < nch) wait_vmcnt<kLtLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if (ci + 2 < nch) issue(ci + 2);
+    const lds_u8* st = smem + (ci % kLsStages) * kLtStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int pc = 2 * ks + half;
+      bf16x8 av[2], bv[3];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = ld_lds_bf16x8(st + xoff[a] + ((pc ^ xsw[a]) * 16));
+#pragma unroll
+      for (int b = 0; b < 3; ++b) bv[b] = ld_lds_bf16x8(st + woff[b] + ((pc ^ wsw[b]) * 16));
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) acc[a][b] = mfma32(av[a], bv[b], acc[a][b]);
+    }
+  }
+
+  // acc[a][b][r]: row m0 + 64 wm + 32a + 8(r/4) + 4*half + r%4,
+  // output n0 + 96 wn + 32b + l32.
+  float* dst = part + (size_t)split * M * N;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (m < M) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) dst[(size_t)m * N + n0 + 96 * wn + 32 * b + l32] = acc[a][b][r];
+      }
+    }
+}
 }  // namespace mla
 
-// Whether the streaming kernel takes an [M, K] x [N, K]^T product.
+// Which kernel takes an [M, K] x [N, K]^T product.
 static bool use_stream(int M, int N, int K) {
   return M >= 1 && M <= 64 && K % mla::kLsKc == 0 && N % 64 == 0;
 }
+static bool use_tile(int M, int N, int K) {
+  return M > 64 && K % mla::kLsKc == 0 && N % mla::kLtBN == 0;
+}
 
-// K slices for an [M, K] x [N, K]^T product.  Streaming kernel: about 384
+// K slices for an [M, K] x [N, K]^T product.  Tile kernel: about 288
+// work-groups, at least 8 chunks per slice.  Streaming kernel: about 384
 // work-groups, at least 4 chunks (256 k) per slice.  Split-K kernel: about
 // 512 waves, at least one k-step (16 values) per slice.  N must be a multiple
 // of 64.
 extern "C" int mla_linear_splits(int M, int N, int K) {
+  if (use_tile(M, N, K)) {
+    // About 288 work-groups, at least 8 chunks (512 k) per slice.
+    const int tiles = (N / mla::kLtBN) * ((M + mla::kLtBM - 1) / mla::kLtBM);
+    const int chunks = K / mla::kLsKc;
+    int s = (288 + tiles - 1) / tiles;
+    const int smax = (chunks + 7) / 8;
+    s = s < 1 ? 1 : (s > smax ? smax : s);
+    const int per = (chunks + s - 1) / s;
+    return (chunks + per - 1) / per;
+  }
   if (use_stream(M, N, K)) {
     const int tiles = (N + mla::kLsN - 1) / mla::kLsN;
     const int chunks = K / mla::kLsKc;
@@ -240,6 +367,19 @@ extern "C" int mla_linear_splits(int M, int N, int K) {
 extern "C" hipError_t mla_launch_linear_splitk(const uint16_t* x, const uint16_t* w, float* part,
                                                int M, int N, int K, int splits,
                                                hipStream_t stream) {
+  if (use_tile(M, N, K)) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&mla::linear_tile_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, mla::kLsStages * mla::kLtStageBytes);
+    if (attr != hipSuccess) return attr;
+    const int chunks = K / mla::kLsKc;
+    int per = (chunks + splits - 1) / splits;
+    void* args[] = {&x, &w, &part, &M, &N, &K, &per};
+    const int tiles = (N / mla::kLtBN) * ((M + mla::kLtBM - 1) / mla::kLtBM);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&mla::linear_tile_kernel),
+                           dim3(tiles * splits), dim3(mla::kLsThreads), args,
+                           mla::kLsStages * mla::kLtStageBytes, stream);
+  }
   if (use_stream(M, N, K)) {
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&mla::linear_stream_kernel),
