@@ -331,17 +331,18 @@ static bool use_tile(int M, int N, int K) {
   return M > 64 && K % mla::kLsKc == 0 && N % mla::kLtBN == 0;
 }
 
-// K slices for an [M, K] x [N, K]^T product.  Tile kernel: about 288
+// K slices for an [M, K] x [N, K]^T product.  Tile kernel: about 192
 // work-groups, at least 8 chunks per slice.  Streaming kernel: about 384
 // work-groups, at least 4 chunks (256 k) per slice.  Split-K kernel: about
 // 512 waves, at least one k-step (16 values) per slice.  N must be a multiple
 // of 64.
 extern "C" int mla_linear_splits(int M, int N, int K) {
   if (use_tile(M, N, K)) {
-    // About 288 work-groups, at least 8 chunks (512 k) per slice.
+    // About 192 work-groups (fewer K slices beat more work-groups here: the
+    // slices' partial sums are traffic too), at least 8 chunks (512 k) per slice.
     const int tiles = (N / mla::kLtBN) * ((M + mla::kLtBM - 1) / mla::kLtBM);
     const int chunks = K / mla::kLsKc;
-    int s = (288 + tiles - 1) / tiles;
+    int s = (192 + tiles - 1) / tiles;
     const int smax = (chunks + 7) / 8;
     s = s < 1 ? 1 : (s > smax ? smax : s);
     const int per = (chunks + s - 1) / s;
