@@ -50,7 +50,8 @@ __device__ __forceinline__ int vt_pos(int t) {
 // Reconstruction
 // ===========================================================================
 constexpr int kWkPitch = 64 + 8;     // bf16 per W_UK LDS row (144 B)
-constexpr int kWvPitch = 128 + 24;   // bf16 per W_UV LDS row (304 B)
+constexpr int kWvPitch = 128 + 32;   // bf16 per W_UV LDS row (320 B: rows 16 banks apart,
+                                     // so the 4 rows of a transposed read hit disjoint banks)
 constexpr int kWkSlice = 128 * kWkPitch;   // bf16 per W_UK slice buffer
 constexpr int kWvSlice = 64 * kWvPitch;    // bf16 per W_UV slice buffer
 
