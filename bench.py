@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection mode: K decode steps plus a 1 GiB device copy "
                          "(the byte-count calibration for HBM counters), nothing else")
+    ap.add_argument("--profile-all", action="store_true",
+                    help="with --profile: also K calls of each secondary workload (prefill, "
+                         "cache append, projections)")
     return ap.parse_args()
 
 
@@ -300,8 +303,15 @@ def main():
         src.fill_(1)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+        if args.profile_all:
+            bench_prefill(args.steps, args.warmup)
+            bench_append(args.steps, args.warmup)
+            bench_projections(args.steps, args.warmup)
+            torch.cuda.synchronize()
         print(json.dumps({"profile": True, "steps": args.warmup + args.steps,
-                          "kv_bytes_per_decode": kv_tokens * ROW_BYTES, "copy_bytes": 1 << 30}))
+                          "kv_bytes_per_decode": kv_tokens * ROW_BYTES, "copy_bytes": 1 << 30,
+                          "secondary": bool(args.profile_all)}))
         return
 
     for _ in range(args.warmup):
