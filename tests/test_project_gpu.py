@@ -36,6 +36,23 @@ def test_output_project(m):
                   f"W_O m={m}")
 
 
+@pytest.mark.parametrize("m,d_in,d_out", [
+    (3, 80, 128),       # K not a multiple of 64: direct-load split-K kernel
+    (64, 64, 320),      # streaming kernel, one 64-k chunk, a partly used 256-output tile
+    (65, 64, 192),      # tile kernel, one chunk, a ragged 128-row tile
+    (130, 448, 384),    # tile kernel, 7 chunks, two output tiles
+    (100, 96, 128),     # M > 64, N not a multiple of 192: split-K kernel
+])
+def test_output_project_kernel_paths(m, d_in, d_out):
+    """Each of the three projection kernels (and their edges) against the oracle."""
+    print(f"[case] output projection m={m} d_in={d_in} d_out={d_out}", flush=True)
+    o, w_o = synth.output_inputs(m, d_in=d_in, d_out=d_out, seed=2520 + m)
+    y = api.output_project(to_dev(o), to_dev(w_o))
+    torch.cuda.synchronize()
+    assert_parity(bf16_to_f64(y), oracle.projections.output_project(f64(o), f64(w_o)),
+                  f"W_O m={m} {d_in}->{d_out}")
+
+
 def test_attention_block_decode_step():
     """x -> query projection -> absorb -> paged decode -> combine -> W_O, four
     sequences, against the oracle chain (un-absorbed attention in fp64).  The
