@@ -15,7 +15,8 @@
 namespace mla {
 
 constexpr int kAbsThreads = 256;
-constexpr int kAbsPitch = 128 + 16;   // bf16 per LDS row (288 B: rows start 8 banks apart)
+constexpr int kAbsPitch = 128 + 32;   // bf16 per LDS row (320 B: rows 16 banks apart, so the
+                                      // 4 rows of a transposed read hit disjoint banks)
 
 __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_c,
                                                                const uint16_t* __restrict__ w_uk,

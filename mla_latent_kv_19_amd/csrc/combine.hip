@@ -19,7 +19,8 @@ namespace mla {
 
 constexpr int kCmbThreads = 256;
 constexpr int kOPitch = 512 + 8;     // bf16 per o_lat LDS row (1040 B)
-constexpr int kWPitch = 128 + 16;    // bf16 per W_UV LDS row (288 B)
+constexpr int kWPitch = 128 + 32;    // bf16 per W_UV LDS row (320 B: rows 16 banks apart,
+                                     // so the 4 rows of a transposed read hit disjoint banks)
 
 __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
