@@ -125,10 +125,12 @@ def cpu_baseline(wl, inp_meta, budget_s):
         n_seq += 1
         if spent * (n_seq + 1) / n_seq > budget_s:
             break
+    total = int(np.sum(inp_meta["seq_lens"]))
     return {"value": tokens / spent, "unit": "KV-tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_seq} of {wl.batch} sequences (all {wl.heads} heads, "
-                      f"{tokens} KV tokens), un-absorbed fp64 numpy oracle, {spent:.1f} s"}
+                      f"{tokens} KV tokens), un-absorbed fp64 numpy oracle, {spent:.1f} s",
+            "extrapolated_full_config_s": total * spent / tokens}
 
 
 def _timed_cold(fn, steps, warmup):
@@ -150,6 +152,19 @@ def _timed_cold(fn, steps, warmup):
     torch.cuda.synchronize()
     del flush
     return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
+def read_probe(nbytes, reps=5):
+    """Measured HBM read rate on this machine: the library's read probe over a
+    buffer of `nbytes` (the decode kernel's KV stream size), each call cold,
+    mean GB/s over `reps` calls."""
+    import torch
+    from mla_latent_kv_19_amd import api
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms = _timed_cold(lambda: api.hbm_read_probe(buf, sink), reps, 1)
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def bench_prefill(steps, warmup):
@@ -398,6 +413,7 @@ def main():
     value = kv_tokens / (ms_step * 1e-3)
     achieved = kv_bytes / (t_decode * 1e-3) / 1e9
     traffic = measured_traffic(kv_bytes)
+    probe_gbs = read_probe(kv_bytes)
     res = {
         "metric": METRIC,
         "value": value,
@@ -433,6 +449,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes,
             "mfma_tflops": kv_tokens * Tq * FLOP_PER_TOKEN_QUERY / (t_decode * 1e-3) / 1e12,
+            "read_probe_gbs": probe_gbs,
+            "frac_of_read_probe": achieved / probe_gbs,
         },
         "wall_s": wall,
         "input_gen_s": gen_s,

@@ -234,6 +234,19 @@ size_t mla_prefill_workspace_bytes(int B, int max_blocks_per_seq, int block_size
 int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size,
                           int num_cus);
 
+/*
+ * Measurement utility, not part of the attention path: reads `bytes` of
+ * device memory at `buf` once, grid-stride with 16-byte loads from every
+ * compute unit, and folds them into one word that is written to `*sink`
+ * (device memory, 4 bytes) only if it equals a magic value, so the reads
+ * cannot be elided.  Timed around a cold call, it gives the HBM read rate
+ * this part delivers to a plain read, which the decode kernel's rate is
+ * reported against beside the published peak.  `buf` must be 16-byte
+ * aligned and `bytes` a positive multiple of 16: MLA_ERR_INVALID_ARG
+ * otherwise.
+ */
+int mla_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

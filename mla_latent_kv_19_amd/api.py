@@ -28,7 +28,7 @@ EXPORTED = (
     "mla_prefill", "mla_decode_part_o_bytes", "mla_decode_part_lse_bytes",
     "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
     "mla_cache_append_workspace_bytes", "mla_query_project", "mla_query_project_workspace_bytes",
-    "mla_output_project", "mla_output_project_workspace_bytes",
+    "mla_output_project", "mla_output_project_workspace_bytes", "mla_hbm_read_probe",
 )
 
 
@@ -76,6 +76,7 @@ def load():
     lib.mla_query_project_workspace_bytes.argtypes = [I, I, I]
     lib.mla_query_project_workspace_bytes.restype = Z
     lib.mla_output_project.argtypes = [P, P, P, P, Z, I, I, I, P]
+    lib.mla_hbm_read_probe.argtypes = [P, Z, P, P]
     lib.mla_output_project.restype = I
     lib.mla_output_project_workspace_bytes.argtypes = [I, I, I]
     lib.mla_output_project_workspace_bytes.restype = Z
@@ -128,6 +129,20 @@ def num_splits(batch, tq, max_seq_len, num_cus=None):
     if s <= 0:
         raise ValueError("invalid arguments to mla_decode_num_splits")
     return s
+
+
+def hbm_read_probe(buf, sink=None):
+    """One read pass over the device tensor `buf` (16-byte aligned, a multiple of
+    16 bytes long) with the library's HBM read probe; returns the 4-byte sink."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    dev = _same_device(buf, sink)
+    _check("mla_hbm_read_probe", load().mla_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink),
+                                                            _stream(dev)))
+    return sink
 
 
 def absorb_q(q_c, w_uk, out=None):

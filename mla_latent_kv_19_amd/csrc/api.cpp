@@ -26,6 +26,8 @@ extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_
                                          int B, int T, int max_blocks, float softmax_scale,
                                          hipStream_t stream);
 
+extern "C" hipError_t mla_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
+                                                hipStream_t stream);
 extern "C" int mla_linear_splits(int M, int N, int K);
 extern "C" hipError_t mla_launch_cache_append(const uint16_t* x, const uint16_t* w_kv,
                                               const uint16_t* gamma, const int32_t* seq_idx,
@@ -77,6 +79,12 @@ const char* mla_strerror(int status) {
 }
 
 int mla_version(void) { return 100; }
+
+int mla_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return MLA_ERR_INVALID_ARG;
+  return status_of(mla_launch_hbm_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
 
 int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat, int M, int H, int d_h,
                  int d_c, void* stream) {

@@ -163,8 +163,13 @@ def test_cache_append_workspace_bytes():
     # One token: the K split fills the chip, each slice a [1, 576] fp32 partial.
     one = lib.mla_cache_append_workspace_bytes(1, 7168)
     assert one % (576 * 4) == 0 and 1 <= one // (576 * 4) <= 7168 // 16
-    # Many tokens: no split needed.
-    assert lib.mla_cache_append_workspace_bytes(4096, 7168) == 4096 * 576 * 4
+    # Many tokens: a few K slices of [4096, 576] fp32 partials, each slice at
+    # least 8 chunks of 64 (the tile kernel's minimum), matching the split
+    # count the library launches with.
+    many = lib.mla_cache_append_workspace_bytes(4096, 7168)
+    slice_bytes = 4096 * 576 * 4
+    assert many % slice_bytes == 0 and 1 <= many // slice_bytes <= 7168 // 512
+    assert many // slice_bytes == lib.mla_linear_splits(4096, 576, 7168)
 
 
 def test_projection_argument_errors():
@@ -211,3 +216,14 @@ def test_projection_workspace_bytes():
     assert lib.mla_query_project_workspace_bytes(64, 7168, 1536) >= 64 * 128 * 192 * 4
     assert lib.mla_output_project_workspace_bytes(4, 100, 7168) == 0
     assert lib.mla_output_project_workspace_bytes(4096, 16384, 7168) == 4096 * 7168 * 4
+
+
+def test_hbm_read_probe_argument_errors():
+    """Validated on the host before any launch: no GPU needed."""
+    lib = _lib()
+    E = api.MLA_ERR_INVALID_ARG
+    assert lib.mla_hbm_read_probe(None, 1024, 16, None) == E            # no buffer
+    assert lib.mla_hbm_read_probe(4096, 1024, None, None) == E          # no sink
+    assert lib.mla_hbm_read_probe(4096, 0, 16, None) == E               # empty
+    assert lib.mla_hbm_read_probe(4096, 1000, 16, None) == E            # not a multiple of 16
+    assert lib.mla_hbm_read_probe(4100, 1024, 16, None) == E            # not 16-byte aligned
