@@ -16,12 +16,12 @@
 //   prefill_attn_kernel out[b,i,h,:] = softmax(q . k * scale, causal) V
 //
 // Work decomposition (MI355X):
-//   * reconstruction: one work-group per (sequence, head, 128 positions); the
-//     128x512 latent block is an MFMA operand read straight from the paged
-//     cache, W_UK[h] and W_UV[h] are staged through LDS in 64-row slices; the
-//     outputs leave through LDS as whole 16-byte chunks of contiguous rows
-//     (a 128-position block of K_C and two 64-key V^T tiles are each one
-//     contiguous 32 KB range);
+//   * reconstruction: one work-group of 8 waves per (sequence, head, 256
+//     positions); the 256x512 latent block is an MFMA operand read straight
+//     from the paged cache, W_UK[h] and W_UV[h] are staged through LDS in
+//     64-row slices; the outputs leave through LDS as whole 16-byte chunks of
+//     contiguous rows (a 256-position block of K_C and four 64-key V^T tiles
+//     are each one contiguous 64 KB range);
 //   * attention: one work-group of 8 waves (2 per SIMD) per (sequence, head,
 //     256 queries), wave w owning 32 queries; 64-key tiles ([K_C | k_R] and
 //     V^T) stream into LDS with direct-to-LDS loads through a 3-stage ring; S^T = K Q^T and
@@ -31,7 +31,8 @@
 
 namespace mla {
 
-constexpr int kPfThreads = 256;
+constexpr int kPfThreads = 512;                   // 8 waves
+constexpr int kPfPos = 256;                       // cached positions per work-group
 
 // ---------------------------------------------------------------------------
 // Key order inside V^T rows.  P^T comes out of the score product with lane
@@ -55,21 +56,29 @@ constexpr int kWvPitch = 128 + 32;   // bf16 per W_UV LDS row (320 B: rows 16 ba
 constexpr int kWkSlice = 128 * kWkPitch;   // bf16 per W_UK slice buffer
 constexpr int kWvSlice = 64 * kWvPitch;    // bf16 per W_UV slice buffer
 
-// Two work-groups per CU (two waves per SIMD) so one hides the other's waits;
-// the weight slices are double buffered through registers.
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
+// LDS: the two weight-slice buffers (76 KB), reused after the products for the
+// output staging (a 256-position K_C block and four V^T tiles, 128 KB).
+constexpr int kKvWBytes = 2 * (kWkSlice + kWvSlice) * 2;
+constexpr int kKvLdsBytes = 2 * kPfPos * 128 * 2;
+static_assert(kKvWBytes <= kKvLdsBytes && kKvLdsBytes <= 160 * 1024, "reconstruction LDS");
+
+// One work-group of 8 waves (two per SIMD) per 256 positions: the 256 KB of
+// W_UK[h] and W_UV[h] a work-group streams through LDS serve 256 positions.
+// The weight slices are double buffered through registers.
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_kv_kernel(
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ w_uk,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ ws_k, uint16_t* __restrict__ ws_vt,
     int max_blocks, int n_tblk) {
-  __shared__ __attribute__((aligned(16))) uint16_t wk[2 * kWkSlice];   // [i][j slice] x 2
-  __shared__ __attribute__((aligned(16))) uint16_t wv[2 * kWvSlice];   // [j slice][d] x 2
+  extern __shared__ __attribute__((aligned(16))) unsigned char kv_smem[];
+  uint16_t* wk = reinterpret_cast<uint16_t*>(kv_smem);   // [i][j slice] x 2
+  uint16_t* wv = wk + 2 * kWkSlice;                      // [j slice][d] x 2
 
   const int tblk = blockIdx.x % n_tblk;
   const int h = (blockIdx.x / n_tblk) % 128;
   const int b = blockIdx.x / (n_tblk * 128);
   const int L = seq_lens[b];
-  const int t0 = tblk * 128;
+  const int t0 = tblk * kPfPos;
   if (t0 >= L) return;
   const int Lpad = max_blocks * 64;
 
@@ -98,31 +107,27 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
   // supplies rows j = 16*ks + 8*(g/2) + q/4 (+4), columns 32n + 16*(g%2) + 4*(q%4).
   const int wv_rd = ((8 * half + (q16 >> 2)) * kWvPitch + 16 * colhalf + 4 * (q16 & 3)) * 2;
 
-  // Slice jc (j = 64jc .. 64jc+63) of both weights: 8 sixteen-byte chunks per
+  // Slice jc (j = 64jc .. 64jc+63) of both weights: 4 sixteen-byte chunks per
   // thread, global -> registers -> LDS.  Thread chunk k: W_UK row (ch / 8),
-  // W_UV row (ch / 16), ch = 256k + tid.
-  const uint16_t* wk_src[4];
-  const uint16_t* wv_src[4];
-  int wk_dst[4], wv_dst[4];
+  // W_UV row (ch / 16), ch = 512k + tid.
+  const uint16_t* wk_src[2];
+  const uint16_t* wv_src[2];
+  int wk_dst[2], wv_dst[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2; ++k) {
     const int ch = k * kPfThreads + tid;
     wk_src[k] = wuk + (size_t)(ch >> 3) * 512 + (ch & 7) * 8;
     wv_src[k] = wuv + (size_t)(ch >> 4) * 128 + (ch & 15) * 8;
     wk_dst[k] = (ch >> 3) * kWkPitch + (ch & 7) * 8;
     wv_dst[k] = (ch >> 4) * kWvPitch + (ch & 15) * 8;
   }
-  uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+  uint4 sk0, sk1, sv0, sv1;
 #define MLA_PF_LOAD_SLICE(jc)                                                       \
   do {                                                                              \
     sk0 = *reinterpret_cast<const uint4*>(wk_src[0] + 64 * (jc));                   \
     sk1 = *reinterpret_cast<const uint4*>(wk_src[1] + 64 * (jc));                   \
-    sk2 = *reinterpret_cast<const uint4*>(wk_src[2] + 64 * (jc));                   \
-    sk3 = *reinterpret_cast<const uint4*>(wk_src[3] + 64 * (jc));                   \
     sv0 = *reinterpret_cast<const uint4*>(wv_src[0] + (size_t)64 * 128 * (jc));     \
     sv1 = *reinterpret_cast<const uint4*>(wv_src[1] + (size_t)64 * 128 * (jc));     \
-    sv2 = *reinterpret_cast<const uint4*>(wv_src[2] + (size_t)64 * 128 * (jc));     \
-    sv3 = *reinterpret_cast<const uint4*>(wv_src[3] + (size_t)64 * 128 * (jc));     \
   } while (0)
 #define MLA_PF_STORE_SLICE(buf)                                                     \
   do {                                                                              \
@@ -130,12 +135,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
     uint16_t* wvb = wv + (buf) * kWvSlice;                                          \
     *reinterpret_cast<uint4*>(wkb + wk_dst[0]) = sk0;                               \
     *reinterpret_cast<uint4*>(wkb + wk_dst[1]) = sk1;                               \
-    *reinterpret_cast<uint4*>(wkb + wk_dst[2]) = sk2;                               \
-    *reinterpret_cast<uint4*>(wkb + wk_dst[3]) = sk3;                               \
     *reinterpret_cast<uint4*>(wvb + wv_dst[0]) = sv0;                               \
     *reinterpret_cast<uint4*>(wvb + wv_dst[1]) = sv1;                               \
-    *reinterpret_cast<uint4*>(wvb + wv_dst[2]) = sv2;                               \
-    *reinterpret_cast<uint4*>(wvb + wv_dst[3]) = sv3;                               \
   } while (0)
 
   bf16x8 a[4];
@@ -185,8 +186,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
   //   V^T      [2 tiles][128 dims][8 chunks of 8 keys], chunk c at c ^ ((d >> 1) & 7),
   //            keys in vt_pos() order inside each 16-key group.
   __syncthreads();
-  lds_u8* kst = to_lds(wk);                    // 32 KB of the 36 KB W_UK buffers
-  lds_u8* vst = to_lds(wv);                    // 32 KB of the 38 KB W_UV buffers
+  lds_u8* kst = to_lds(kv_smem);                       // 64 KB K_C block
+  lds_u8* vst = to_lds(kv_smem) + kPfPos * 256;        // four 16 KB V^T tiles
   {
     const int pk = 32 * wave + l32;            // this lane's K position in the block
     const bool k_ok = t0 + pk < L;
@@ -219,8 +220,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kv_kernel(
   }
   __syncthreads();
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  // 2048 chunks of each output per work-group, 8 per thread.  Positions past
-  // Lpad (the last 128-block may overhang by one 64-key tile) are not stored.
+  // 4096 chunks of each output per work-group, 8 per thread.  Positions past
+  // Lpad (the last 256-block may overhang by up to three 64-key tiles) are not
+  // stored.
   uint16_t* kdst = ws_k + ((size_t)(b * 128 + h) * Lpad + t0) * 128;
   uint16_t* vdst = ws_vt + ((size_t)(b * 128 + h) * Lpad + t0) * 128;   // tile t0 / 64
 #pragma unroll
@@ -477,11 +479,16 @@ extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_
   const size_t Lpad = (size_t)max_blocks * 64;
   uint16_t* ws_k = static_cast<uint16_t*>(workspace);
   uint16_t* ws_vt = ws_k + (size_t)B * 128 * Lpad * 128;
-  int n_tblk = (int)((Lpad + 127) / 128);
+  int n_tblk = (int)((Lpad + mla::kPfPos - 1) / mla::kPfPos);
   {
+    static const hipError_t kv_attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&mla::prefill_kv_kernel),
+        hipFuncAttributeMaxDynamicSharedMemorySize, mla::kKvLdsBytes);
+    if (kv_attr != hipSuccess) return kv_attr;
     void* args[] = {&kv, &block_table, &seq_lens, &w_uk, &w_uv, &ws_k, &ws_vt, &max_blocks, &n_tblk};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&mla::prefill_kv_kernel),
-                                         dim3(B * 128 * n_tblk), dim3(mla::kPfThreads), args, 0, stream);
+                                         dim3(B * 128 * n_tblk), dim3(mla::kPfThreads), args,
+                                         mla::kKvLdsBytes, stream);
     if (e != hipSuccess) return e;
   }
   int n_qblk = (T + mla::kQBlock - 1) / mla::kQBlock;
