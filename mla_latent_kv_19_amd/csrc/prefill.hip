@@ -368,10 +368,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
   for (int n = 0; n < 4; ++n) acc[n] = f32x16{};
   float m_ref = -INFINITY, l_run = 0.f;
 
-  // Per-lane LDS read offsets.
-  const int kq_swz = k_swz(l32);                 // key row l32 (+32 for the second tile)
-  const int vt_row = l32;                        // V^T row d = 32n + l32
-  const int vq_swz = v_swz(vt_row);
+  // Per-lane LDS read offsets within a stage.  The swizzle leaves four
+  // distinct lane offsets per operand kind; the rest of each address is an
+  // immediate.  K: key row l32 (+32 for the second half of the tile), k-step
+  // ks = 4q + r reads chunk 8q + ((2r + half) ^ k_swz(l32)).  V^T: row d =
+  // 32n + l32, 16-key step k reads chunk (2k + half) ^ v_swz(l32).
+  int koff[4], voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    koff[r] = l32 * kKRowChunks * 16 + (((2 * r + half) ^ k_swz(l32)) * 16);
+    voff[r] = kKTileBytes + l32 * kVRowChunks * 16 + (((2 * r + half) ^ v_swz(l32)) * 16);
+  }
 
   for (int i = 0; i < n_tiles; ++i) {
     lds_u8* cur = smem + (i % kRingStages) * kStageBytes;
@@ -387,12 +394,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x16{};
-      const lds_u8* krow = cur + (kt * 32 + l32) * kKRowChunks * 16;
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) {
-        const int c = 2 * ks + half;
-        const int p = (c & ~7) | ((c & 7) ^ kq_swz);
-        s[kt] = mfma32(ld_lds_bf16x8(krow + p * 16), qreg[ks], s[kt]);
+        const lds_u8* kp = cur + koff[ks & 3] + kt * 32 * kKRowChunks * 16 + (ks >> 2) * 128;
+        s[kt] = mfma32(ld_lds_bf16x8(kp), qreg[ks], s[kt]);
       }
     }
     // s[kt][r]: key k0 + 32kt + 8*(r/4) + 4*half + r%4, query qi.
@@ -436,14 +441,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
       pb[r >> 3][r & 7] = (__bf16)p;
     }
     // O^T[128 d x 32 q] += V^T[128 x 16 keys] . P^T over four 16-key steps.
-    const lds_u8* vt = cur + kKTileBytes + vt_row * kVRowChunks * 16;
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
-      const int c = 2 * kstep + half;            // 8 keys of this lane's half
-      const int p = c ^ vq_swz;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const bf16x8 av = ld_lds_bf16x8(vt + (32 * n * kVRowChunks + p) * 16);
+        const bf16x8 av = ld_lds_bf16x8(cur + voff[kstep] + 32 * n * kVRowChunks * 16);
         acc[n] = mfma32(av, pb[kstep], acc[n]);
       }
     }
