@@ -6,7 +6,7 @@
 //   part[s, m, n] = sum over k in K slice s of x[m, k] * w[n, k]
 //
 // x is [M, K] and w is a linear layer's [N, K] weight, both bf16 and
-// k-contiguous.  Two kernels, one output contract (the callers' finish
+// k-contiguous.  Three kernels, one output contract (the callers' finish
 // kernels sum the slices):
 //  * linear_stream_kernel, M <= 64 (a decode batch), K a multiple of 64: the
 //    weight is the traffic.  A work-group of 4 waves takes 256 outputs and a
