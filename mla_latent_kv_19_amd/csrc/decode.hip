@@ -16,17 +16,21 @@
 //   * each wave keeps its 32 latent queries (512 wide, bf16) in 128 VGPRs as the
 //     B operand (the 64-wide rotary queries of all heads sit in LDS) and its
 //     output O^T (512 x 32 heads, fp32) in the 256 AGPRs;
-//   * per 32-token tile: S^T[32 tok x 32 heads] = K[32 x 576] . Q^T as two
-//     independent MFMA 32x32x16 chains (even / odd k-steps), online softmax in
-//     registers (lane = head), then O^T[512 x 32] += V^T[512 x 32 tok] . P^T
+//   * per 32-token tile: S^T[32 tok x 32 heads] = K[32 x 576] . Q^T as one
+//     chain of 36 MFMA 32x32x16, online softmax in registers (lane = head), then O^T[512 x 32] += V^T[512 x 32 tok] . P^T
 //     (32 MFMA; V^T read from the same LDS tile with transposed reads, P^T is the
 //     score registers reinterpreted: no shuffles);
 //   * software pipeline: the score MFMAs of tile n, then the value MFMAs of
 //     tile n-1 with the softmax of tile n issued in pieces between them;
 //   * tiles stream global -> LDS with 16-byte direct-to-LDS loads through a ring
 //     of 4 stages (2 in flight while 2 are being multiplied), one barrier per
-//     tile; the loads of a tile are spread over the score MFMAs of the tile two
-//     ahead.
+//     tile; wave w loads rows 8w .. 8w+7 of a tile, in 9 pieces spread over the
+//     score MFMAs of the tile two ahead, with scalar addresses only;
+//   * the score mask runs only on the (at most two) tiles that reach past the
+//     query's last visible key; the loop over all other tiles has no mask and
+//     no per-load test.
+#include <type_traits>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -60,9 +64,7 @@ static_assert(qk_piece(33) == 8 && qk_piece(35) == -1, "nine pieces over 36 k-st
 // the row.  On the 64-bank LDS both access patterns are conflict-free: 16
 // consecutive rows reading one chunk (score operand, 16 lanes per cycle) and 4
 // consecutive rows x 4 adjacent chunks (transposed value reads, 32 lanes per
-// cycle).  Because one 64-lane direct-to-LDS load fills exactly one block, each
-// lane's source offset depends only on its lane id and the parity of the row
-// group: the per-tile address work is two scalar adds per load.
+// cycle).  One 64-lane direct-to-LDS load fills exactly one block.
 __device__ __forceinline__ int row_swz(int t) {
   return (((t >> 1) & 1) << 2) | (((t >> 2) & 1) << 1) | ((t >> 3) & 1);
 }
@@ -74,28 +76,46 @@ __device__ __forceinline__ int tile_off(int t, int c) {
   return (t >> 3) * kRowGrpBytes + (c >> 3) * kBlkBytes + (t & 7) * 128 + ((c & 7) ^ row_swz(t)) * 16;
 }
 
-// All 256 threads: copy 32 consecutive cache rows into an LDS stage, one of 9
-// pieces per call.  Wave w fills blocks 4*it + w; lane j of a block loads row
-// 8*(block/9) + j/8, chunk 8*(block%9) + ((j%8) ^ swizzle).  o0 / o1 are the
-// lane's offsets for even / odd row groups.  Every direct-to-LDS load of this
-// kernel goes through the opaque form (the kernel sets M0 only there).
-__device__ __forceinline__ void issue_piece(const char* g, lds_u8* stage, int wave, int it, int o0,
-                                            int o1) {
-  const int blk = it * 4 + wave;                 // wave-uniform
-  const int rg = blk / 9, cb = blk - rg * 9;
-  g2lds16_opaque(g + rg * 8 * kRowBytes + cb * 128 + ((rg & 1) ? o1 : o0), stage + blk * kBlkBytes);
+// Copy of a 32-row tile into an LDS stage: wave w loads row group w (rows
+// 8w .. 8w+7, the 9 blocks (w, 0..8) of 1 KB) in 9 pieces.  Lane j of piece IT
+// loads row 8w + j/8, chunk 8 IT + ((j%8) ^ swizzle); its byte offset inside the
+// row group (voff) depends only on the lane and the parity of w, so the
+// per-tile address work is scalar: the row group's global address is one SGPR
+// pair (gw) and each piece adds 128 IT bytes as the instruction's immediate
+// offset.  That offset is added to the LDS destination as well (M0 + offset +
+// 16 x lane), so M0 = stage_w + 1024 IT - 128 IT puts piece IT at block IT.
+// The load is inline asm with M0 set here: as a builtin it is a FLAT
+// instruction that may write LDS, after which the compiler makes every later
+// LDS wait lgkmcnt(0) and serialises the operand reads issued ahead; the
+// hardware counts it in vmcnt only, which the kernel waits on explicitly.
+template <int IT>
+__device__ __forceinline__ void load_piece(const char* gw, int voff, lds_u8* stage_w) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>(stage_w)));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(gw);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32));
+  const unsigned long long sb = (static_cast<unsigned long long>(hi) << 32) | lo;
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%4"
+               :
+               : "v"(voff), "s"(sb), "s"(m0), "n"(IT * (kBlkBytes - 128)), "n"(IT * 128)
+               : "m0");
 }
-
-__device__ __forceinline__ void issue_tile(const uint16_t* rows, lds_u8* stage, int wave,
-                                           const int (&src_lane)[2]) {
-  const char* g = reinterpret_cast<const char*>(rows);
-  // Opaque copies: keeps the compiler from precomputing (and spilling) nine
-  // 64-bit addresses across the tile loop; each load costs one 64-bit add.
-  int o0 = src_lane[0], o1 = src_lane[1];
-  asm volatile("" : "+v"(o0), "+v"(o1));
-#pragma unroll
-  for (int it = 0; it < kLoadsPerThread; ++it) issue_piece(g, stage, wave, it, o0, o1);
+// Piece `it` (a compile-time constant at every call site once unrolled).
+__device__ __forceinline__ void issue_piece(int it, const char* gw, int voff, lds_u8* stage_w) {
+  switch (it) {
+    case 0: load_piece<0>(gw, voff, stage_w); break;
+    case 1: load_piece<1>(gw, voff, stage_w); break;
+    case 2: load_piece<2>(gw, voff, stage_w); break;
+    case 3: load_piece<3>(gw, voff, stage_w); break;
+    case 4: load_piece<4>(gw, voff, stage_w); break;
+    case 5: load_piece<5>(gw, voff, stage_w); break;
+    case 6: load_piece<6>(gw, voff, stage_w); break;
+    case 7: load_piece<7>(gw, voff, stage_w); break;
+    default: load_piece<8>(gw, voff, stage_w); break;
+  }
 }
+static_assert(kLoadsPerThread == 9 && kDecThreads / 64 * 8 == kTileTok, "one row group per wave, 9 pieces");
 
 __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_r,
@@ -123,11 +143,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   const int l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = wave * 32 + l32;
-  int src_lane[2];
+  // Source offset of this lane's 16 bytes inside its wave's row group: row
+  // lane/8, chunk (lane%8) ^ row_swz(row), where bit 0 of the swizzle is the
+  // parity of the row group (= wave).
+  int voff;
   {
-    const int f = (((lane >> 4) & 1) << 2) | (((lane >> 5) & 1) << 1);
-    src_lane[0] = (lane >> 3) * kRowBytes + ((lane & 7) ^ f) * 16;
-    src_lane[1] = (lane >> 3) * kRowBytes + ((lane & 7) ^ (f | 1)) * 16;
+    const int f = (((lane >> 4) & 1) << 2) | (((lane >> 5) & 1) << 1) | (wave & 1);
+    voff = (lane >> 3) * kRowBytes + ((lane & 7) ^ f) * 16;
   }
 
   const int L = seq_lens[b];
@@ -160,8 +182,17 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     const int t = T0 + n * kTileTok;                  // a tile never crosses a cache block
     return kv + ((size_t)table[t >> 6] * kTok + (t & (kTok - 1))) * kRowVals;
   };
-  issue_tile(tile_rows(0), smem, wave, src_lane);
-  if (ntiles > 1) issue_tile(tile_rows(1), smem + kTileBytes, wave, src_lane);
+  {
+    const char* g0 = reinterpret_cast<const char*>(tile_rows(0)) + wave * 8 * kRowBytes;
+#pragma unroll
+    for (int it = 0; it < kLoadsPerThread; ++it) issue_piece(it, g0, voff, smem + wave * kRowGrpBytes);
+    if (ntiles > 1) {
+      const char* g1 = reinterpret_cast<const char*>(tile_rows(1)) + wave * 8 * kRowBytes;
+#pragma unroll
+      for (int it = 0; it < kLoadsPerThread; ++it)
+        issue_piece(it, g1, voff, smem + kTileBytes + wave * kRowGrpBytes);
+    }
+  }
 
   // Rotary queries of all 128 heads -> LDS, [head][64] with the 8 chunks of a
   // row XOR-swizzled by bits 1..3 of the head (16 consecutive heads reading one
@@ -212,9 +243,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   // nine direct-to-LDS loads per wave would stall the wave at issue while the
   // address unit drains the other waves' loads.
   struct Next {
-    const char* g;
-    lds_u8* stage;
-    int o0, o1;
+    const char* g;       // this wave's row group of tile n+2, or null
+    lds_u8* stage;       // its LDS destination
   };
   auto top = [&](int n, Next& nx) {
     // Tile n has landed for every wave, every wave is done with tile n-2, whose
@@ -223,11 +253,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     lds_barrier();
     nx.g = nullptr;
     if (n + 2 < ntiles) {
-      nx.g = reinterpret_cast<const char*>(tile_rows(n + 2));
-      nx.stage = smem + ((n + 2) % kRing) * kTileBytes;
-      nx.o0 = src_lane[0];
-      nx.o1 = src_lane[1];
-      asm volatile("" : "+v"(nx.o0), "+v"(nx.o1));
+      nx.g = reinterpret_cast<const char*>(tile_rows(n + 2)) + wave * 8 * kRowBytes;
+      nx.stage = smem + ((n + 2) % kRing) * kTileBytes + wave * kRowGrpBytes;
     }
     const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
     if (valid < kTileTok) {
@@ -269,13 +296,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     float mx = -INFINITY, m_use = 0.f, sum = 0.f, mxs = 0.f, arg = 0.f;
     bool move = false;
   };
-  auto sm_step = [&](int k, int lim, Softmax& st, const f32x16& sp, bf16x8 (&pb)[2], float& alpha,
+  auto sm_step = [&](auto MASK, int k, int lim, Softmax& st, const f32x16& sp, bf16x8 (&pb)[2], float& alpha,
                      bool& resc) {
     if (k < 8) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * k + e;
-        st.x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
+        if constexpr (decltype(MASK)::value) st.x[r] = (8 * (r >> 2) + (r & 3) < lim) ? sp[r] : -INFINITY;
+        else st.x[r] = sp[r];
         st.mx = fmaxf(st.mx, st.x[r]);
       }
     } else if (k == 8) {
@@ -307,33 +335,31 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   };
   auto tile_lim = [&](int n) { return n_vis - (T0 + n * kTileTok + 4 * half); };
 
-  // Score product of tile n, two independent MFMA chains (even / odd k-steps),
-  // with the nine loads of tile n+2 (if any) spread over it.  sched_barrier
+  // Score product of tile n, one MFMA chain over the 36 k-steps, with the nine
+  // loads of tile n+2 spread over it (LD: the caller knows there is a tile
+  // n+2, so the loads are issued without a test).  sched_barrier
   // fences pin the order: the LDS reads stay 4 k-steps ahead of their MFMA.
   // The MFMAs are compiler builtins (VGPR form), so the compiler inserts every
   // wait state their results need.  Operands rotate through 6 registers: the
   // load issued after MFMA kk refills the one MFMA kk-2 used.
-  auto scores = [&](int n, const Next& nx, f32x16& sn) {
+  auto scores = [&](auto LD, int n, const Next& nx, f32x16& sn) {
     const lds_u8* rd = smem + (n % kRing) * kTileBytes + qk_base;
     bf16x8 kb[6], qrb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = ld_k(rd, j);
-    f32x16 ae = {}, ao = {};
+    f32x16 ae = {};
 #pragma unroll
     for (int kk = 0; kk < 36; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       const bf16x8 qop = (kk < 32) ? qreg[kk] : qrb[kk - 32];
-      if (kk & 1)
-        ao = mfma32(kb[kk % 6], qop, ao);
-      else
-        ae = mfma32(kb[kk % 6], qop, ae);
+      ae = mfma32(kb[kk % 6], qop, ae);
       if (kk + 4 < 36) kb[(kk + 4) % 6] = ld_k(rd, kk + 4);
       if (kk >= 28 && kk < 32) qrb[kk - 28] = ld_qr(kk - 28);
-      if (qk_piece(kk) >= 0 && nx.g != nullptr)
-        issue_piece(nx.g, nx.stage, wave, qk_piece(kk), nx.o0, nx.o1);
+      if (qk_piece(kk) >= 0 && (decltype(LD)::value || nx.g != nullptr))
+        issue_piece(qk_piece(kk), nx.g, voff, nx.stage);
     }
     __builtin_amdgcn_sched_barrier(0);
-    sn = ae + ao;
+    sn = ae;
   };
 
   // Rare rescale, then O^T += V^T . P^T for tile n (32 MFMAs, value operands
@@ -341,7 +367,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   // With a next tile (scores sp), its softmax runs in pieces between the value
   // MFMAs and leaves P, alpha and the rescale flag for the next call in
   // pb2 / alpha2 / resc2.
-  auto rescale_and_pv = [&](int n, bf16x8 (&pb)[2], float alpha, bool resc, bool with_sm,
+  auto rescale_and_pv = [&](auto MASK, int n, bf16x8 (&pb)[2], float alpha, bool resc, bool with_sm,
                             const f32x16& sp, bf16x8 (&pb2)[2], float& alpha2, bool& resc2) {
     valu_to_mfma_settle(pb[0], pb[1]);
     if (__any(resc)) {
@@ -365,7 +391,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                    : "+a"(acc[m & 15]) : "v"(vb[m % 5]), "v"(pb[m >> 4]));
       if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, m + 3);
-      if (with_sm) sm_step(m, lim, st, sp, pb2, alpha2, resc2);
+      if (with_sm) sm_step(MASK, m, lim, st, sp, pb2, alpha2, resc2);
     }
   };
 
@@ -377,21 +403,41 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     f32x16 s0;
     Next nx;
     top(0, nx);
-    scores(0, nx, s0);
+    scores(std::false_type{}, 0, nx, s0);
     Softmax st;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) sm_step(k, tile_lim(0), st, s0, pb, alpha, resc);
+    for (int k = 0; k < 32; ++k) sm_step(std::true_type{}, k, tile_lim(0), st, s0, pb, alpha, resc);
   }
   // ---- steady state: scores(n), then values(n-1) with softmax(n) ----
-  for (int n = 1; n < ntiles; ++n) {
+  // The softmax of tile n runs in iteration n.  Tiles below n_full are visible
+  // to the query in full (no score mask); below n_ld there is also a tile n+2
+  // to load.  The remaining (at most two) iterations run the general form.
+  const int n_full = min(ntiles, (n_vis - T0) / kTileTok);
+  const int n_ld = min(n_full, ntiles - 2);
+  int n = 1;
+  for (; n < n_ld; ++n) {
     Next nx;
     top(n, nx);
     f32x16 sn;
-    scores(n, nx, sn);
+    scores(std::true_type{}, n, nx, sn);
     bf16x8 pb2[2];
     float alpha2;
     bool resc2;
-    rescale_and_pv(n - 1, pb, alpha, resc, true, sn, pb2, alpha2, resc2);
+    rescale_and_pv(std::false_type{}, n - 1, pb, alpha, resc, true, sn, pb2, alpha2, resc2);
+    pb[0] = pb2[0];
+    pb[1] = pb2[1];
+    alpha = alpha2;
+    resc = resc2;
+  }
+  for (; n < ntiles; ++n) {
+    Next nx;
+    top(n, nx);
+    f32x16 sn;
+    scores(std::false_type{}, n, nx, sn);
+    bf16x8 pb2[2];
+    float alpha2;
+    bool resc2;
+    rescale_and_pv(std::true_type{}, n - 1, pb, alpha, resc, true, sn, pb2, alpha2, resc2);
     pb[0] = pb2[0];
     pb[1] = pb2[1];
     alpha = alpha2;
@@ -401,7 +447,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     bf16x8 pd[2];
     float ad;
     bool rd;
-    rescale_and_pv(ntiles - 1, pb, alpha, resc, false, f32x16{}, pd, ad, rd);
+    rescale_and_pv(std::false_type{}, ntiles - 1, pb, alpha, resc, false, f32x16{}, pd, ad, rd);
   }
 
   agpr_settle16(acc);
