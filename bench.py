@@ -9,7 +9,9 @@ the shapes of the pages' model (128 heads, latent 512 + rotary 64, content
 head 128) and are resident in HBM before timing starts.  Each timed step is
 bracketed by its own HIP events; a 512 MiB read before each step (outside
 the events) leaves no cache state from the previous step.  ms_per_step is the
-mean over the timed steps, with p10 / p50 / p90 alongside.
+mean over the timed steps, with p10 / p50 / p90 alongside.  The default 30
+warm-up steps let the clock settle after the start of sustained load (a
+transient in which the same launch runs up to ~1.5x slower).
 
 Prints one JSON line: whole-job throughput in KV-tokens/s, the dominant
 kernel's roofline position (algorithmic bytes / measured launch time against
@@ -57,8 +59,11 @@ class _Flush:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 30 warm-up steps (~20 ms of sustained load): the GPU's clock management
+    # settles only after a transient in which the same decode launch runs up to
+    # ~1.5x slower; timing 60 steps then averages over its remaining swings.
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--splits", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
