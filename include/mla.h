@@ -188,8 +188,10 @@ size_t mla_cache_append_workspace_bytes(int M, int d_model);
  * x bf16 [M, d_model]; w_dq bf16 [q_rank, d_model]; gamma_q bf16 [q_rank];
  * w_uq bf16 [H * (d_h + d_r), q_rank]; positions int32 [M] (device, >= 0);
  * q_c bf16 [M, H, d_h] and q_r bf16 [M, H, d_r] out (the inputs of
- * mla_absorb_q and mla_decode_paged).  c_q' is rounded to bf16 between the
- * two products.  workspace: mla_query_project_workspace_bytes(M, d_model,
+ * mla_absorb_q and mla_decode_paged).  RMSNorm's per-row factor is applied
+ * after the second product (it commutes with it): gamma_q * c_q is rounded to
+ * bf16 between the two products and the fp32 result of the second is scaled
+ * by 1 / sqrt(mean(c_q^2) + eps).  workspace: mla_query_project_workspace_bytes(M, d_model,
  * q_rank) bytes, 256-byte aligned.
  * Supported: H = 128, d_h = 128, d_r = 64, d_model a multiple of 16, q_rank a
  * multiple of 256 up to 4096 (7168 and 1536 in DeepSeek-V3).

@@ -12,9 +12,13 @@
 //   y = W_O o                           (128 x 128 -> 7168)
 //
 // Each product is the split-K projection of linear.hip; the kernels here sum
-// its K slices and apply what follows the product: RMSNorm (one work-group per
-// row), the per-head split and RoPE (64 lanes per head), or a plain bf16
-// rounding.
+// its K slices and apply what follows the product: RMSNorm, the per-head split
+// and RoPE (64 lanes per head), or a plain bf16 rounding.  RMSNorm's per-row
+// factor commutes with the second product, so it is applied after it:
+//   W_UQ (gamma * c_q / rms) = (W_UQ (gamma * c_q)) / rms,
+// and the sum over c_q's K slices runs as one wave per 256 columns, writing
+// bf16(gamma * c_q) and the block's sum of squares; the split + RoPE kernel
+// then scales by 1 / rms of its row.
 #include <cmath>
 
 #include "mla_common.h"
@@ -33,74 +37,73 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-// One work-group of 256 threads per row: out[m, :] = bf16(RMSNorm(sum_s part[s, m, :]) * gamma).
-// N is a multiple of 256 (at most 4096).
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ part,
-                                                           int splits, int M, int N,
-                                                           const uint16_t* __restrict__ gamma,
-                                                           float eps, uint16_t* __restrict__ out) {
-  __shared__ float red[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  const int per = N / 256;                       // values per thread: n = tid + 256 j
-  float v[16];
+// One wave per (row m, 256 columns): c = sum_s part[s, m, n] over the K
+// slices (16-byte loads, 16 slices in flight per lane), cq[m, n] =
+// bf16(gamma[n] * c) and ssq[m, blk] = sum over the block's columns of c^2.
+// N is a multiple of 256.
+__global__ __launch_bounds__(64) void qnorm_sum_kernel(const float* __restrict__ part, int splits,
+                                                       int M, int N,
+                                                       const uint16_t* __restrict__ gamma,
+                                                       uint16_t* __restrict__ cq,
+                                                       float* __restrict__ ssq) {
+  const int nb = N / 256;
+  const int m = blockIdx.x / nb, blk = blockIdx.x - m * nb;
+  const int n = blk * 256 + 4 * threadIdx.x;
+  const size_t stride = (size_t)M * N;
+  const float* p = part + (size_t)m * N + n;
+  float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    float4 t[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = 0.f;
-  // K slices four at a time, so that up to 64 loads per thread are in flight.
-  int s = 0;
-  for (; s + 4 <= splits; s += 4) {
-    float t[4][16];
+    for (int u = 0; u < 16; ++u)
+      t[u] = (s0 + u < splits) ? *reinterpret_cast<const float4*>(p + (size_t)(s0 + u) * stride)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float* p = part + ((size_t)(s + u) * M + m) * N + tid;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) t[u][j] = (j < per) ? p[256 * j] : 0.f;
+    for (int u = 0; u < 16; ++u) {
+      c.x += t[u].x;
+      c.y += t[u].y;
+      c.z += t[u].z;
+      c.w += t[u].w;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] += t[u][j];
   }
-  for (; s < splits; ++s) {
-    const float* p = part + ((size_t)s * M + m) * N + tid;
+  bf16x4 o;
+  o[0] = (__bf16)(c.x * bf16_to_f32(gamma[n]));
+  o[1] = (__bf16)(c.y * bf16_to_f32(gamma[n + 1]));
+  o[2] = (__bf16)(c.z * bf16_to_f32(gamma[n + 2]));
+  o[3] = (__bf16)(c.w * bf16_to_f32(gamma[n + 3]));
+  *reinterpret_cast<bf16x4*>(cq + (size_t)m * N + n) = o;
+  float q = c.x * c.x + c.y * c.y + c.z * c.z + c.w * c.w;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < per) v[j] += p[256 * j];
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < per) ss += v[j] * v[j];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
-  const float inv_rms = 1.f / sqrtf(tot / N + eps);
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < per) {
-      const int n = tid + 256 * j;
-      out[(size_t)m * N + n] = f32_to_bf16(v[j] * inv_rms * bf16_to_f32(gamma[n]));
-    }
+  for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off);
+  if (threadIdx.x == 0) ssq[blockIdx.x] = q;
 }
 
 // Per (row m, head h): 64 lanes.  Lane l sums columns 192h + l and 192h + 64 + l
 // (content query) and 192h + 128 + l (rotary query, rotated with its pair
-// partner l ^ 1).  Work-group = 4 heads of one row.
+// partner l ^ 1), then scales by the row's 1 / rms (from the nb block sums of
+// squares of c_q, over q_rank values).  Work-group = 4 heads of one row.
 __global__ __launch_bounds__(256) void qsplit_rope_kernel(
     const float* __restrict__ part, int splits, int M, int H, const int32_t* __restrict__ positions,
-    double log_theta, uint16_t* __restrict__ q_c, uint16_t* __restrict__ q_r) {
+    double log_theta, const float* __restrict__ ssq, int nb, int q_rank, float eps,
+    uint16_t* __restrict__ q_c, uint16_t* __restrict__ q_r) {
   const int m = blockIdx.x / (H / 4);
   const int h = (blockIdx.x % (H / 4)) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int N = H * 192;
   float a = 0.f, b = 0.f, r = 0.f;
+#pragma unroll 4
   for (int s = 0; s < splits; ++s) {
     const float* p = part + ((size_t)s * M + m) * N + 192 * h + lane;
     a += p[0];
     b += p[64];
     r += p[128];
   }
+  float ss = 0.f;
+  for (int k = 0; k < nb; ++k) ss += ssq[m * nb + k];
+  const float inv_rms = 1.f / sqrtf(ss / q_rank + eps);
+  a *= inv_rms;
+  b *= inv_rms;
+  r *= inv_rms;
   const int pos = positions[m];
   const int i = lane >> 1;
   const double ang = fmod((double)pos * exp(-(2.0 * i / 64.0) * log_theta), 6.283185307179586);
@@ -137,11 +140,14 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
 
 }  // namespace mla
 
-// Workspace layout of the query projection: c_q' (bf16 [M, q_rank], rounded
-// up to 256 bytes), then the K-slice partials of whichever product is running
-// (the first product's are consumed before the second's are written).
+// Workspace layout of the query projection: gamma * c_q (bf16 [M, q_rank]),
+// the block sums of squares (fp32 [M, q_rank / 256]), each rounded up to 256
+// bytes, then the K-slice partials of whichever product is running (the
+// first product's are consumed before the second's are written).
+static size_t qp_cq_bytes(int M, int q_rank) { return (((size_t)M * q_rank * 2) + 255) / 256 * 256; }
+static size_t qp_ssq_bytes(int M, int q_rank) { return (((size_t)M * (q_rank / 256) * 4) + 255) / 256 * 256; }
 extern "C" size_t mla_query_project_ws(int M, int d_model, int q_rank, int H) {
-  const size_t cq = (((size_t)M * q_rank * 2) + 255) / 256 * 256;
+  const size_t cq = qp_cq_bytes(M, q_rank) + qp_ssq_bytes(M, q_rank);
   const size_t p1 = (size_t)mla_linear_splits(M, q_rank, d_model) * M * q_rank * 4;
   const size_t p2 = (size_t)mla_linear_splits(M, H * 192, q_rank) * M * H * 192 * 4;
   return cq + (p1 > p2 ? p1 : p2);
@@ -154,15 +160,17 @@ extern "C" hipError_t mla_launch_query_project(const uint16_t* x, const uint16_t
                                                int q_rank, int H, float eps, float theta,
                                                hipStream_t stream) {
   uint16_t* cq = static_cast<uint16_t*>(workspace);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         (((size_t)M * q_rank * 2) + 255) / 256 * 256);
+  float* ssq = reinterpret_cast<float*>(static_cast<char*>(workspace) + qp_cq_bytes(M, q_rank));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + qp_cq_bytes(M, q_rank) +
+                                         qp_ssq_bytes(M, q_rank));
   int s1 = mla_linear_splits(M, q_rank, d_model);
   hipError_t e = mla_launch_linear_splitk(x, w_dq, part, M, q_rank, d_model, s1, stream);
   if (e != hipSuccess) return e;
+  int nb = q_rank / 256;
   {
-    void* args[] = {&part, &s1, &M, &q_rank, &gamma_q, &eps, &cq};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&mla::rmsnorm_rows_kernel), dim3(M),
-                        dim3(256), args, 0, stream);
+    void* args[] = {&part, &s1, &M, &q_rank, &gamma_q, &cq, &ssq};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&mla::qnorm_sum_kernel), dim3(M * nb),
+                        dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   const int n2 = H * 192;
@@ -170,7 +178,7 @@ extern "C" hipError_t mla_launch_query_project(const uint16_t* x, const uint16_t
   e = mla_launch_linear_splitk(cq, w_uq, part, M, n2, q_rank, s2, stream);
   if (e != hipSuccess) return e;
   double log_theta = std::log((double)theta);
-  void* args[] = {&part, &s2, &M, &H, &positions, &log_theta, &q_c, &q_r};
+  void* args[] = {&part, &s2, &M, &H, &positions, &log_theta, &ssq, &nb, &q_rank, &eps, &q_c, &q_r};
   return hipLaunchKernel(reinterpret_cast<const void*>(&mla::qsplit_rope_kernel),
                          dim3(M * (H / 4)), dim3(256), args, 0, stream);
 }
