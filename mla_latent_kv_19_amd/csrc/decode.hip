@@ -308,9 +308,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       }
     } else if (k == 8) {
       // maximum over lanes l and l^32 (the two halves of one head's tokens)
-      const unsigned v = __builtin_bit_cast(unsigned, st.mx);
-      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-      st.mx = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+      st.mx = pair32_max(st.mx);
     } else if (k == 9) {
       st.mxs = st.mx * scale_log2;                 // log2 units
       st.move = st.mxs > m_ref + kLazy;

@@ -184,4 +184,27 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Maximum / sum of v over lanes l and l ^ 32 (the two halves of a row of an
+// MFMA 32x32 result), in every lane, with v_permlane32_swap (a VALU exchange,
+// no LDS round trip): the swap exchanges the upper half of its first register
+// with the lower half of its second, so with both holding v the two hold
+// [v_lo, v_lo] and [v_hi, v_hi], and one max / add gives the pair's result in
+// every lane.  Written as inline asm: through the compiler builtin, the
+// optimiser folds the builtin's second result into its first (a max of the two
+// then returns the lower half's value), a miscompilation seen with this
+// toolchain.  The s_nop's give the wait states between a VALU write and the
+// swap's read, and between the swap and the VALU read of its results.
+__device__ __forceinline__ float pair32_max(float v) {
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_add_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a);
+}
+
 }  // namespace mla

@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
           mx = fmaxf(mx, x[16 * kt + r]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;      // log2 units
+    mx = pair32_max(mx) * scale_log2;     // over lanes l, l^32 (one query's keys); log2 units
     const bool move = mx > m_ref + 8.f;
     if (move) {
       const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mx);
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair32_sum(l_run);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (q_ok) {
     uint16_t* dst = out + (((size_t)b * T + qi) * 128 + h) * 128;

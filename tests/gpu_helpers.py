@@ -72,3 +72,18 @@ def assert_parity(got, ref, what, max_abs=MAX_ABS, rel_l2=REL_L2):
 
 def make(wl, seq_lens=None):
     return synth.make_inputs(wl, seq_lens=seq_lens)
+
+
+def plant_dominant_keys(inp, keys, scale=40.0, seed=7):
+    """Make key t of sequence b dominate every score that sees it, for each
+    (b, t) in `keys`: all heads and queries of sequence b get the same rotary
+    query u (N(0, 1), 64 wide) and token t's rotary key becomes scale * u, so
+    its score exceeds the others by about scale * 64 / sqrt(192) (natural
+    units).  Edits the bf16 bit arrays of `inp` in place."""
+    rng = np.random.default_rng(seed)
+    for b, t in keys:
+        u = rng.standard_normal(64).astype(np.float32)
+        inp.q_r[b] = synth.f32_to_bf16_bits(u)
+        blk = inp.block_table[b, t // 64]
+        inp.kv_cache[blk, t % 64, 512:576] = synth.f32_to_bf16_bits(np.float32(scale) * u)
+    return inp

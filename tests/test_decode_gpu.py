@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from gpu_helpers import (DevInputs, assert_parity, bf16_to_f64, make, oracle_decode,
-                         run_decode, to_dev)
+                         plant_dominant_keys, run_decode, to_dev)
 from mla_latent_kv_19_amd import api, synth
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +84,20 @@ def test_edge_lengths(tq, lens):
     print(f"[case] edge lengths tq={tq} lens={lens}", flush=True)
     wl = synth.small_workload(batch=len(lens), tq=tq, len_lo=1, len_hi=1, seed=41 + tq)
     _check_decode(make(wl, seq_lens=lens), what=f"edge lengths tq={tq}")
+
+
+@pytest.mark.parametrize("tq", [1, 2])
+def test_dominant_key(tq):
+    """One key per sequence whose score exceeds every other by about 185
+    (natural units): the softmax puts all weight on it and the output is its
+    value row.  The keys sit at tile positions 4, 8 and 5 (token % 32), i.e. in
+    both halves of the kernel's lane split of a 32-token tile, so the running
+    maximum has to span both halves: a maximum taken over one half would leave
+    the other's exponent at ~2^267 and overflow."""
+    print(f"[case] dominant key tq={tq}", flush=True)
+    wl = synth.small_workload(batch=3, tq=tq, len_lo=tq, len_hi=tq, seed=61 + tq)
+    inp = plant_dominant_keys(make(wl, seq_lens=[300, 150, 120]), [(0, 36), (1, 40), (2, 101)])
+    _check_decode(inp, what=f"dominant key tq={tq}")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DevInputs, assert_parity, bf16_to_f64, make
+from gpu_helpers import DevInputs, assert_parity, bf16_to_f64, make, plant_dominant_keys
 from mla_latent_kv_19_amd import api, synth
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,18 @@ def test_full_prefill_small(lens):
     inp = make(wl, seq_lens=lens)
     got = _run_prefill(DevInputs(inp))
     assert_parity(got, _oracle_prefill(inp), f"prefill T=L={T}")
+
+
+def test_prefill_dominant_key():
+    """A key whose score exceeds every other by about 185 (natural units): queries
+    at or after it put all weight on it (output = its value row), earlier ones do
+    not see it.  Keys at tile positions 4 and 5 (token % 8 in 4..7: the upper half
+    of the kernel's lane split of a key tile) and 8 (lower half)."""
+    print("[case] prefill dominant key", flush=True)
+    wl = synth.small_workload(batch=3, tq=200, len_lo=200, len_hi=200, seed=111, prefill=True)
+    inp = plant_dominant_keys(make(wl, seq_lens=[200, 200, 200]), [(0, 36), (1, 101), (2, 40)])
+    got = _run_prefill(DevInputs(inp))
+    assert_parity(got, _oracle_prefill(inp), "prefill dominant key")
 
 
 @pytest.mark.parametrize("T,lens", [(40, [150, 300, 77]), (1, [5, 64, 129]), (129, [129, 200])])
