@@ -87,3 +87,28 @@ def plant_dominant_keys(inp, keys, scale=40.0, seed=7):
         blk = inp.block_table[b, t // 64]
         inp.kv_cache[blk, t % 64, 512:576] = synth.f32_to_bf16_bits(np.float32(scale) * u)
     return inp
+
+
+def plant_rescale_jump(inp, b, n_old, n_new, jump=6.0, seed=11):
+    """Sequence b: latent queries q_C = 0 and rotary keys 0 for every token
+    except n_new tokens starting at n_old, so all other scores are exactly 0;
+    those n_new tokens get rotary key s * u (rotary query u for every head and
+    query) with s chosen so that their score is about `jump` (natural units).
+    With jump = 6 (8.7 in log2 units) the running maximum moves past a 2^8
+    lazy-rescale threshold once, while the n_old earlier tokens keep a large
+    share of the softmax mass (n_old against n_new * e^jump), so the rescale of
+    what was accumulated before the jump decides the output.  Edits `inp` in
+    place."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(64).astype(np.float32)
+    ub = synth.f32_to_bf16_bits(u)
+    uf = synth.bf16_bits_to_f64(ub)
+    s = jump / (float(uf @ uf) * inp.wl.scale)
+    inp.q_c[b] = 0
+    inp.q_r[b] = ub
+    L = int(inp.seq_lens[b])
+    kb = synth.f32_to_bf16_bits(np.float32(s) * u)
+    for t in range(L):
+        blk = inp.block_table[b, t // 64]
+        inp.kv_cache[blk, t % 64, 512:576] = kb if n_old <= t < n_old + n_new else 0
+    return inp

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DevInputs, assert_parity, bf16_to_f64, make, plant_dominant_keys
+from gpu_helpers import (DevInputs, assert_parity, bf16_to_f64, make, plant_dominant_keys,
+                         plant_rescale_jump)
 from mla_latent_kv_19_amd import api, synth
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +48,20 @@ def test_prefill_dominant_key():
     inp = plant_dominant_keys(make(wl, seq_lens=[200, 200, 200]), [(0, 36), (1, 101), (2, 40)])
     got = _run_prefill(DevInputs(inp))
     assert_parity(got, _oracle_prefill(inp), "prefill dominant key")
+
+
+def test_prefill_lazy_rescale():
+    """Queries after a jump of the running maximum past the lazy-rescale
+    threshold, with the earlier keys still carrying most of the mass (2560 keys
+    of score 0, then 2 of score ~6): heads 0 and 77 against the oracle, every
+    query."""
+    print("[case] prefill lazy rescale", flush=True)
+    T = 2700
+    wl = synth.small_workload(batch=1, tq=T, len_lo=T, len_hi=T, seed=121, prefill=True)
+    inp = plant_rescale_jump(make(wl), 0, 2560, 2)
+    got = _run_prefill(DevInputs(inp))
+    heads = [0, 77]
+    assert_parity(got[:, :, heads], _oracle_prefill(inp, heads=heads), "prefill lazy rescale")
 
 
 @pytest.mark.parametrize("T,lens", [(40, [150, 300, 77]), (1, [5, 64, 129]), (129, [129, 200])])
