@@ -64,23 +64,45 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     MLA_CMB_W_DST(3) = wr3; MLA_CMB_W_DST(4) = wr4; MLA_CMB_W_DST(5) = wr5;  \
     MLA_CMB_W_DST(6) = wr6; MLA_CMB_W_DST(7) = wr7;                          \
   } while (0)
-  MLA_CMB_LOAD_W(0);
 
-  // 1. Split weights per row.
+  // 1. Split weights per row.  All threads load the split log-sum-exps (four
+  // each, unconditionally from clamped addresses), then the first W_UV slice is
+  // put in flight, then the log-sum-exps go to LDS (wts has at least 1024
+  // slots, so the stores need no test and the loads cannot be moved into one)
+  // and one thread per row normalises them: one memory round trip for up to
+  // 32 splits.
+  const int n_l = S * 32;
+  float lv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + k * kCmbThreads;
+    const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), M - 1);
+    lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
+  }
+  MLA_CMB_LOAD_W(0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + k * kCmbThreads;
+    wts[i] = (i < n_l && m0 + (i & 31) < M) ? lv[k] : -INFINITY;
+  }
+  for (int i = tid + 4 * kCmbThreads; i < n_l; i += kCmbThreads) {
+    const int sp = i >> 5, r = i & 31;
+    wts[i] = (m0 + r < M) ? part_lse[sp * split_stride + (size_t)(m0 + r) * 128 + h] : -INFINITY;
+  }
+  __syncthreads();
   if (tid < 32) {
     const int m = m0 + tid;
     float mx = -INFINITY;
-    if (m < M)
-      for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_lse[s * split_stride + (size_t)m * 128 + h]);
+    for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, wts[sp * 32 + tid]);
     float z = 0.f;
     if (mx != -INFINITY)
-      for (int s = 0; s < S; ++s) {
-        const float w = __expf(part_lse[s * split_stride + (size_t)m * 128 + h] - mx);
-        wts[s * 32 + tid] = w;
+      for (int sp = 0; sp < S; ++sp) {
+        const float w = __expf(wts[sp * 32 + tid] - mx);
+        wts[sp * 32 + tid] = w;
         z += w;
       }
     const float inv = (z > 0.f) ? 1.f / z : 0.f;
-    for (int s = 0; s < S; ++s) wts[s * 32 + tid] = (mx != -INFINITY) ? wts[s * 32 + tid] * inv : 0.f;
+    for (int sp = 0; sp < S; ++sp) wts[sp * 32 + tid] = (mx != -INFINITY) ? wts[sp * 32 + tid] * inv : 0.f;
     if (lse_out != nullptr && m < M)
       lse_out[(size_t)m * 128 + h] = (mx != -INFINITY) ? mx + __logf(z) : -INFINITY;
   }
@@ -168,7 +190,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 }
 
 size_t combine_lds_bytes(int S) {
-  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)S * 32 * 4;
+  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)(S > 32 ? S : 32) * 32 * 4;
 }
 
 }  // namespace mla
