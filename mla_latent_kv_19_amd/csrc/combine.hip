@@ -108,34 +108,38 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   }
   __syncthreads();
 
-  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2k,
-  // four rows at a time (the partials of four rows and up to four splits in
-  // flight together).
+  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2u,
+  // eight rows at a time (two iterations), so that the partials of eight rows
+  // and two splits are in flight together.  A split of weight 0 (empty, whose
+  // partial may hold anything) is dropped by a select, not a branch.
   {
     const int cq = tid & 127;
-    for (int r0 = tid >> 7; r0 < 32; r0 += 8) {
-      float4 o[4];
+#pragma unroll 1
+    for (int r0 = tid >> 7; r0 < 32; r0 += 16) {
+      float4 o[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+      for (int u = 0; u < 8; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
       for (int s = 0; s < S; ++s) {
-        float4 v[4];
+        float4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const int m = min(m0 + r0 + 2 * u, M - 1);
           v[u] = *reinterpret_cast<const float4*>(part_o + (s * split_stride + (size_t)m * 128 + h) * 512 +
                                                   4 * cq);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           const float w = (m0 + r0 + 2 * u < M) ? wts[s * 32 + r0 + 2 * u] : 0.f;
-          if (w != 0.f) {          // an empty split may hold -inf/NaN-free zeros; skip it anyway
-            o[u].x += w * v[u].x; o[u].y += w * v[u].y; o[u].z += w * v[u].z; o[u].w += w * v[u].w;
-          }
+          const bool use = w != 0.f;
+          o[u].x += use ? w * v[u].x : 0.f;
+          o[u].y += use ? w * v[u].y : 0.f;
+          o[u].z += use ? w * v[u].z : 0.f;
+          o[u].w += use ? w * v[u].w : 0.f;
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int r = r0 + 2 * u;
         const float ov[4] = {o[u].x, o[u].y, o[u].z, o[u].w};
         bf16x4 hi, lo;
