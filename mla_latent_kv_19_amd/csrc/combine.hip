@@ -41,29 +41,33 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   const int wave = tid >> 6;
   const size_t split_stride = (size_t)M * 128;   // rows of one split
 
-  // W_UV[h] rows 128jc .. 128jc+127 (128 x 16 sixteen-byte chunks), staged
-  // through registers: the loads of slice 0 are issued first, to overlap the
-  // split merge below, and each next slice's during the current one's product.
+  // W_UV[h] rows 128jc .. 128jc+127 (slice jc: 128 x 16 sixteen-byte chunks),
+  // staged through registers, three slices deep: slice 0 is loaded first (it
+  // overlaps the split merge below), slices 1 and 2 right after the merge,
+  // slice 3 once slice 0 is in LDS (slices 0 and 3 in w0, 1 in w1, 2 in w2).
   const uint16_t* wsrc = w_uv + (size_t)h * 512 * 128;
-  uint4 wr0, wr1, wr2, wr3, wr4, wr5, wr6, wr7;
-#define MLA_CMB_W_SRC(k, jc) \
-  (*reinterpret_cast<const uint4*>(wsrc + (size_t)((jc) * 128 + (((k) * kCmbThreads + tid) >> 4)) * 128 + \
-                                   (((k) * kCmbThreads + tid) & 15) * 8))
-#define MLA_CMB_W_DST(k) \
-  (*reinterpret_cast<uint4*>(&wt[(((k) * kCmbThreads + tid) >> 4) * kWPitch + (((k) * kCmbThreads + tid) & 15) * 8]))
-#define MLA_CMB_LOAD_W(jc)                                                   \
-  do {                                                                       \
-    wr0 = MLA_CMB_W_SRC(0, jc); wr1 = MLA_CMB_W_SRC(1, jc);                  \
-    wr2 = MLA_CMB_W_SRC(2, jc); wr3 = MLA_CMB_W_SRC(3, jc);                  \
-    wr4 = MLA_CMB_W_SRC(4, jc); wr5 = MLA_CMB_W_SRC(5, jc);                  \
-    wr6 = MLA_CMB_W_SRC(6, jc); wr7 = MLA_CMB_W_SRC(7, jc);                  \
-  } while (0)
-#define MLA_CMB_STORE_W()                                                    \
-  do {                                                                       \
-    MLA_CMB_W_DST(0) = wr0; MLA_CMB_W_DST(1) = wr1; MLA_CMB_W_DST(2) = wr2;  \
-    MLA_CMB_W_DST(3) = wr3; MLA_CMB_W_DST(4) = wr4; MLA_CMB_W_DST(5) = wr5;  \
-    MLA_CMB_W_DST(6) = wr6; MLA_CMB_W_DST(7) = wr7;                          \
-  } while (0)
+  // Eight named chunks (not an array, which the compiler would keep in
+  // scratch memory).
+  struct WSlice {
+    uint4 c0, c1, c2, c3, c4, c5, c6, c7;
+  };
+  auto w_src = [&](int jc, int k) {
+    const int c = k * kCmbThreads + tid;
+    return *reinterpret_cast<const uint4*>(wsrc + (size_t)(jc * 128 + (c >> 4)) * 128 + (c & 15) * 8);
+  };
+  auto w_dst = [&](int k) -> uint4& {
+    const int c = k * kCmbThreads + tid;
+    return *reinterpret_cast<uint4*>(&wt[(c >> 4) * kWPitch + (c & 15) * 8]);
+  };
+  auto load_w = [&](int jc, WSlice& d) {
+    d.c0 = w_src(jc, 0); d.c1 = w_src(jc, 1); d.c2 = w_src(jc, 2); d.c3 = w_src(jc, 3);
+    d.c4 = w_src(jc, 4); d.c5 = w_src(jc, 5); d.c6 = w_src(jc, 6); d.c7 = w_src(jc, 7);
+  };
+  auto store_w = [&](const WSlice& d) {
+    w_dst(0) = d.c0; w_dst(1) = d.c1; w_dst(2) = d.c2; w_dst(3) = d.c3;
+    w_dst(4) = d.c4; w_dst(5) = d.c5; w_dst(6) = d.c6; w_dst(7) = d.c7;
+  };
+  WSlice w0, w1, w2;
 
   // 1. Split weights per row.  All threads load the split log-sum-exps (four
   // each, unconditionally from clamped addresses), then the first W_UV slice is
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), M - 1);
     lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
   }
-  MLA_CMB_LOAD_W(0);
+  load_w(0, w0);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = tid + k * kCmbThreads;
@@ -161,13 +165,10 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
                       ((8 * half + (q16 >> 2)) * kWPitch + 32 * wave + 16 * colhalf + 4 * (q16 & 3)) * 2;
   const lds_u8* ahb = to_lds(o_hi) + (l32 * kOPitch + 8 * half) * 2;
   const lds_u8* alb = to_lds(o_lo) + (l32 * kOPitch + 8 * half) * 2;
+  load_w(1, w1);
+  load_w(2, w2);
   f32x16 acc = {};
-#pragma unroll
-  for (int jc = 0; jc < 4; ++jc) {
-    __syncthreads();                 // every wave is done with the previous slice
-    MLA_CMB_STORE_W();
-    __syncthreads();
-    if (jc + 1 < 4) MLA_CMB_LOAD_W(jc + 1);
+  auto product = [&](int jc) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x4 blo = ld_lds_tr(trb + (16 * ks) * kWPitch * 2);
@@ -177,11 +178,25 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
       acc = mfma32(ld_lds_bf16x8(ahb + koff), bw, acc);
       acc = mfma32(ld_lds_bf16x8(alb + koff), bw, acc);
     }
-  }
-#undef MLA_CMB_W_SRC
-#undef MLA_CMB_W_DST
-#undef MLA_CMB_LOAD_W
-#undef MLA_CMB_STORE_W
+  };
+  // Each slice: every wave is done with the previous one, then it goes to LDS.
+  __syncthreads();
+  store_w(w0);
+  __syncthreads();
+  load_w(3, w0);
+  product(0);
+  __syncthreads();
+  store_w(w1);
+  __syncthreads();
+  product(1);
+  __syncthreads();
+  store_w(w2);
+  __syncthreads();
+  product(2);
+  __syncthreads();
+  store_w(w0);
+  __syncthreads();
+  product(3);
   // acc[r]: row m0 + 8*(r/4) + 4*half + r%4, column 32*wave + l32.
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
