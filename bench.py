@@ -203,6 +203,60 @@ def bench_prefill(steps, warmup):
             "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flop": flops}
 
 
+def bench_decode_configs(steps, warmup):
+    """The other decode workloads (single sequence, batched ragged, two-token
+    MTP verify, long context): one full step each (absorb, split-KV attention,
+    combine), cold-timed, placed against its binding roofline by arithmetic
+    intensity.  Algorithmic bytes: KV rows + W_UK + W_UV + queries + outputs;
+    FLOP: attention over every (query, visible key) pair + absorb + W_UV."""
+    import torch
+    from mla_latent_kv_19_amd import api, synth
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    res = {}
+    for name in ("single", "batched", "mtp", "long"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+        B, Tq = wl.batch, wl.tq
+        lens = inp.seq_lens.astype(np.int64)
+        q_c, q_r, kv = dev(inp.q_c), dev(inp.q_r), dev(inp.kv_cache)
+        table = torch.from_numpy(inp.block_table).cuda()
+        lens_d = torch.from_numpy(inp.seq_lens).cuda()
+        w_uk, w_uv = dev(inp.w_uk), dev(inp.w_uv)
+        del inp
+        splits = api.num_splits(B, Tq, int(lens.max()))
+        q_lat = torch.empty((B, Tq, 128, 512), dtype=torch.bfloat16, device="cuda")
+        part_o = torch.empty((splits, B, Tq, 128, 512), dtype=torch.float32, device="cuda")
+        part_lse = torch.empty((splits, B, Tq, 128), dtype=torch.float32, device="cuda")
+        out = torch.empty((B, Tq, 128, 128), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            api.absorb_q(q_c, w_uk, out=q_lat)
+            api.decode_paged(q_lat, q_r, kv, table, lens_d, wl.scale, splits, part_o, part_lse)
+            api.combine(part_o, part_lse, w_uv, out=out)
+
+        ms = _timed_cold(step, steps, warmup)
+        rows = int(lens.sum())
+        attended = int(sum(int(L) - Tq + i + 1 for L in lens for i in range(Tq)))
+        nq = B * Tq
+        nbytes = rows * ROW_BYTES + 2 * 128 * 128 * 512 * 2 + nq * 128 * (192 + 128) * 2
+        flops = attended * FLOP_PER_TOKEN_QUERY + 2 * nq * 128 * 2 * 128 * 512
+        secs = ms * 1e-3
+        bound = "hbm" if flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+        frac = (nbytes / secs / 1e9 / HBM_PEAK_GBS if bound == "hbm"
+                else flops / secs / 1e12 / BF16_PEAK_TFLOPS)
+        res[name] = {"workload": f"{wl.name}: {wl.note}", "splits": splits, "ms": ms,
+                     "kv_tokens_per_s": rows / secs, "attended_per_s": attended / secs,
+                     "gbs": nbytes / secs / 1e9, "tflops": flops / secs / 1e12,
+                     "bound": bound, "frac": frac, "algorithmic_bytes": nbytes,
+                     "algorithmic_flop": flops}
+        del q_c, q_r, kv, table, lens_d, w_uk, w_uv, q_lat, part_o, part_lse, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_append(steps, warmup):
     """Cache append (kv_down 7168 -> 576, RMSNorm, RoPE, paged write) for the
     64 new tokens of one decode step and for a 4096-token prefill chunk."""
@@ -460,6 +514,7 @@ def main():
         "wall_s": wall,
         "input_gen_s": gen_s,
     }
+    res["decode_configs"] = bench_decode_configs(max(5, args.steps // 4), 3)
     res["prefill"] = bench_prefill(max(3, args.steps // 4), 2)
     res["cache_append"] = bench_append(max(5, args.steps // 2), 3)
     res["projections"] = bench_projections(max(5, args.steps // 2), 3)
