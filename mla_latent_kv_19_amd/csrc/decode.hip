@@ -182,18 +182,24 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     const int t = T0 + n * kTileTok;                  // a tile never crosses a cache block
     return kv + ((size_t)table[t >> 6] * kTok + (t & (kTok - 1))) * kRowVals;
   };
+
+  // Start-up loads, in this order so that one round trip brings what the first
+  // score product needs: the latent queries (registers), tile 0, the rotary
+  // queries (staged in LDS: waiting for them also waits for everything issued
+  // before, vmcnt being in order), then tile 1, which streams in behind.
+  // Latent queries as B operands: k-step kk covers dims 16kk .. 16kk+15.
+  bf16x8 qreg[32];
+  {
+    const uint16_t* ql = q_lat + row * 512 + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) qreg[kk] = ld_global_bf16x8(ql + 16 * kk);
+  }
+
   {
     const char* g0 = reinterpret_cast<const char*>(tile_rows(0)) + wave * 8 * kRowBytes;
 #pragma unroll
     for (int it = 0; it < kLoadsPerThread; ++it) issue_piece(it, g0, voff, smem + wave * kRowGrpBytes);
-    if (ntiles > 1) {
-      const char* g1 = reinterpret_cast<const char*>(tile_rows(1)) + wave * 8 * kRowBytes;
-#pragma unroll
-      for (int it = 0; it < kLoadsPerThread; ++it)
-        issue_piece(it, g1, voff, smem + kTileBytes + wave * kRowGrpBytes);
-    }
   }
-
   // Rotary queries of all 128 heads -> LDS, [head][64] with the 8 chunks of a
   // row XOR-swizzled by bits 1..3 of the head (16 consecutive heads reading one
   // chunk then hit distinct banks).
@@ -205,12 +211,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     st_lds16(qr_lds + (h * 8 + (c ^ ((h >> 1) & 7))) * 16, v);
   }
 
-  // Latent queries as B operands: k-step kk covers dims 16kk .. 16kk+15.
-  bf16x8 qreg[32];
-  {
-    const uint16_t* ql = q_lat + row * 512 + 8 * half;
+  if (ntiles > 1) {
+    const char* g1 = reinterpret_cast<const char*>(tile_rows(1)) + wave * 8 * kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < 32; ++kk) qreg[kk] = ld_global_bf16x8(ql + 16 * kk);
+    for (int it = 0; it < kLoadsPerThread; ++it)
+      issue_piece(it, g1, voff, smem + kTileBytes + wave * kRowGrpBytes);
   }
 
   f32x16 acc[16];
