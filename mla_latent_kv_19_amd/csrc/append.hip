@@ -13,8 +13,9 @@
 // Two kernels (MI355X):
 //   * the split-K projection of linear.hip (fp32 partial sums per K slice of
 //     the 7168-wide hidden state into the workspace);
-//   * append_finish_kernel: one wave per token: sums the K slices, RMSNorm of
-//     the latent (wave reduction), RoPE of the rotary part (angle reduced in
+//   * append_finish_kernel: four waves per token sum the K slices (every
+//     fourth each, all loads in flight), then one wave does the RMSNorm of the
+//     latent (wave reduction), RoPE of the rotary part (angle reduced in
 //     float64: positions reach 10^5 and more), bf16 rounding, the cache write.
 #include <cmath>
 
@@ -30,37 +31,43 @@ namespace mla {
 constexpr int kAppOut = 576;            // 512 latent + 64 rotary outputs
 constexpr int kAppDc = 512;
 
-__global__ __launch_bounds__(64) void append_finish_kernel(
+__global__ __launch_bounds__(256) void append_finish_kernel(
     const float* __restrict__ part, const uint16_t* __restrict__ gamma,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ block_table, uint16_t* __restrict__ kv, int M, int splits,
     int max_blocks, float eps, double log_theta) {
+  __shared__ float red[4][kAppOut];
   const int m = blockIdx.x;
-  const int lane = threadIdx.x;
-  // Output n = lane + 64j: j < 8 latent, j = 8 rotary value lane.
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Output n = lane + 64j: j < 8 latent, j = 8 rotary value lane.  Wave w sums
+  // slices w, w + 4, ..., eight of them per batch (all 72 loads in flight), so
+  // up to 32 slices take one memory round trip; then wave 0 adds the four.
   float v[9];
 #pragma unroll
   for (int j = 0; j < 9; ++j) v[j] = 0.f;
-  // Slices in groups of 8, so that 72 loads are in flight at once.
-  int s = 0;
-  for (; s + 8 <= splits; s += 8) {
+  for (int s0 = w; s0 < splits; s0 += 32) {
     float t[8][9];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float* p = part + ((size_t)(s + u) * M + m) * kAppOut + lane;
+      const int sl = min(s0 + 4 * u, splits - 1);
+      const float* p = part + ((size_t)sl * M + m) * kAppOut + lane;
 #pragma unroll
       for (int j = 0; j < 9; ++j) t[u][j] = p[64 * j];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = s0 + 4 * u < splits;
 #pragma unroll
-      for (int j = 0; j < 9; ++j) v[j] += t[u][j];
+      for (int j = 0; j < 9; ++j) v[j] += ok ? t[u][j] : 0.f;
+    }
   }
-  for (; s < splits; ++s) {
-    const float* p = part + ((size_t)s * M + m) * kAppOut + lane;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) v[j] += p[64 * j];
-  }
+  for (int j = 0; j < 9; ++j) red[w][lane + 64 * j] = v[j];
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+    v[j] = (red[0][lane + 64 * j] + red[1][lane + 64 * j]) + (red[2][lane + 64 * j] + red[3][lane + 64 * j]);
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
@@ -105,5 +112,5 @@ extern "C" hipError_t mla_launch_cache_append(const uint16_t* x, const uint16_t*
   void* args[] = {&workspace, &gamma, &seq_idx, &positions, &block_table, &kv, &M, &s,
                   &max_blocks, &eps, &log_theta};
   return hipLaunchKernel(reinterpret_cast<const void*>(&mla::append_finish_kernel), dim3(M),
-                         dim3(64), args, 0, stream);
+                         dim3(256), args, 0, stream);
 }
