@@ -122,13 +122,22 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
                                                          uint16_t* __restrict__ out) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= total) return;
+  // Eight slices per batch, all loads in flight (clamped index, then a select:
+  // one load per iteration would make every slice its own round trip).
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < splits; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(part + (size_t)s * total + i);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      t[u] = *reinterpret_cast<const float4*>(part + (size_t)min(s0 + u, splits - 1) * total + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = s0 + u < splits;
+      acc.x += ok ? t[u].x : 0.f;
+      acc.y += ok ? t[u].y : 0.f;
+      acc.z += ok ? t[u].z : 0.f;
+      acc.w += ok ? t[u].w : 0.f;
+    }
   }
   bf16x4 o;
   o[0] = (__bf16)acc.x;
