@@ -332,8 +332,8 @@ static bool use_tile(int M, int N, int K) {
 }
 
 // K slices for an [M, K] x [N, K]^T product.  Tile kernel: about 192
-// work-groups, at least 8 chunks per slice.  Streaming kernel: about 384
-// work-groups, at least 4 chunks (256 k) per slice.  Split-K kernel: about
+// work-groups, at least 8 chunks per slice.  Streaming kernel: at most 256
+// work-groups (one round), at least 4 chunks (256 k) per slice.  Split-K kernel: about
 // 512 waves, at least one k-step (16 values) per slice.  N must be a multiple
 // of 64.
 extern "C" int mla_linear_splits(int M, int N, int K) {
@@ -349,9 +349,13 @@ extern "C" int mla_linear_splits(int M, int N, int K) {
     return (chunks + per - 1) / per;
   }
   if (use_stream(M, N, K)) {
+    // At most one round of work-groups on the 256 compute units (one per CU:
+    // the ring takes 120 KB of LDS): a partial second round leaves most CUs
+    // idle while it runs (W_O 64 x 16384 -> 7168: 9 slices 51 us, 14 slices
+    // 60 us; W_UQ 1536 -> 24576: 2 slices 22 us, 4 slices 26 us).
     const int tiles = (N + mla::kLsN - 1) / mla::kLsN;
     const int chunks = K / mla::kLsKc;
-    int s = (384 + tiles - 1) / tiles;
+    int s = 256 / tiles;
     const int smax = (chunks + 3) / 4;
     s = s < 1 ? 1 : (s > smax ? smax : s);
     const int per = (chunks + s - 1) / s;
