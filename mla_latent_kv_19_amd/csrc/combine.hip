@@ -112,29 +112,50 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   }
   __syncthreads();
 
-  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of rows tid/128 + 2u,
-  // eight rows at a time (two iterations), so that the partials of eight rows
-  // and two splits are in flight together.  A split of weight 0 (empty, whose
-  // partial may hold anything) is dropped by a select, not a branch.
+  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of eight
+  // consecutive rows, r0 .. r0+7 with r0 = 8*(tid/128) (+16 in the second
+  // iteration), so that the partials of eight rows and two splits are in flight
+  // together.  A group of eight rows with none below M is skipped (uniform per
+  // pair of waves): its LDS rows only feed output rows >= M, which are never
+  // written.  When the block has at most eight rows below M, both pairs of
+  // waves work on them, each on every second split, and their fp32 sums meet
+  // in the (not yet used) W_UV staging area.  A split of weight 0 (empty,
+  // whose partial may hold anything) is dropped by a select, not a branch.
   {
-    const int cq = tid & 127;
+    const int cq = tid & 127, hh = tid >> 7;
+    const bool pair = M - m0 <= 8;                      // uniform over the work-group
+    float* scratch = reinterpret_cast<float*>(wt);      // [2][8][512] when pair
+    auto store_hilo = [&](int r, float4 v) {
+      const float ov[4] = {v.x, v.y, v.z, v.w};
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (__bf16)ov[e];
+        lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
+      *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
+    };
 #pragma unroll 1
-    for (int r0 = tid >> 7; r0 < 32; r0 += 16) {
+    for (int it = 0; it < 2; ++it) {
+      const int r0 = pair ? 0 : hh * 8 + 16 * it;
+      if (pair ? it > 0 : m0 + r0 >= M) continue;
+      const int s_first = pair ? hh : 0, s_step = pair ? 2 : 1;
       float4 o[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 2
-      for (int s = 0; s < S; ++s) {
+      for (int s = s_first; s < S; s += s_step) {
         float4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int m = min(m0 + r0 + 2 * u, M - 1);
+          const int m = min(m0 + r0 + u, M - 1);
           v[u] = *reinterpret_cast<const float4*>(part_o + (s * split_stride + (size_t)m * 128 + h) * 512 +
                                                   4 * cq);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float w = (m0 + r0 + 2 * u < M) ? wts[s * 32 + r0 + 2 * u] : 0.f;
+          const float w = (m0 + r0 + u < M) ? wts[s * 32 + r0 + u] : 0.f;
           const bool use = w != 0.f;
           o[u].x += use ? w * v[u].x : 0.f;
           o[u].y += use ? w * v[u].y : 0.f;
@@ -142,18 +163,24 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
           o[u].w += use ? w * v[u].w : 0.f;
         }
       }
+      if (pair) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = r0 + 2 * u;
-        const float ov[4] = {o[u].x, o[u].y, o[u].z, o[u].w};
-        bf16x4 hi, lo;
+        for (int u = 0; u < 8; ++u)
+          *reinterpret_cast<float4*>(&scratch[(hh * 8 + u) * 512 + 4 * cq]) = o[u];
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[e] = (__bf16)ov[e];
-          lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+        for (int u = 0; u < 8; ++u) store_hilo(r0 + u, o[u]);
+      }
+    }
+    if (pair) {
+      __syncthreads();
+      if (hh == 0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float4 a0 = *reinterpret_cast<const float4*>(&scratch[u * 512 + 4 * cq]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&scratch[(8 + u) * 512 + 4 * cq]);
+          store_hilo(u, make_float4(a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w));
         }
-        *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
-        *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
       }
     }
   }
