@@ -123,6 +123,24 @@ def test_split_counts(splits):
     _check_decode(make(wl), splits=splits, what=f"splits={splits}")
 
 
+def test_max_split_count():
+    """num_splits = 256 (the maximum): a 16,384-token sequence in 256 splits of
+    one page each beside a 300-token one whose splits are mostly empty, Tq = 2
+    (the combine reads 256 log-sum-exps per row and merges the non-empty
+    splits).  Against the absorbed fp64 form, which is pinned to the
+    un-absorbed oracle to 1e-12."""
+    print("[case] splits=256", flush=True)
+    wl = synth.small_workload(batch=2, tq=2, len_lo=2, len_hi=2, seed=57)
+    inp = make(wl, seq_lens=[16384, 300])
+    dev = DevInputs(inp)
+    out, lse = run_decode(dev, splits=256)
+    ref, ref_lse = oracle_decode(inp, form="absorbed")
+    assert_parity(bf16_to_f64(out), ref, "splits=256")
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_lse))
+    assert np.max(np.abs(got_lse - ref_lse)) <= 2e-2
+
+
 def test_split_invariance_and_page_permutation():
     print("[case] split invariance / page permutation", flush=True)
     wl = synth.small_workload(batch=5, tq=1, len_lo=1, len_hi=900, seed=61)
