@@ -12,7 +12,10 @@
 // kept in LDS as a bf16 hi/lo pair (o = hi + lo to about 16 bits), so the
 // bf16 MFMA product carries nearly fp32 accuracy of o_lat at twice the (tiny)
 // matrix work.  W_UV[h] is staged through LDS in 128-row slices and read with
-// transposed reads to form the 8-consecutive-j operand layout.
+// transposed reads to form the 8-consecutive-j operand layout.  The split merge
+// skips row groups that lie past M; when a block holds at most eight rows, the
+// two halves of the work-group take alternate splits of the same rows and add
+// their fp32 partial sums in LDS, so few-row decode does not leave half idle.
 #include "mla_common.h"
 
 namespace mla {
