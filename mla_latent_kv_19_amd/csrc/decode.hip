@@ -17,10 +17,9 @@
 //     B operand (the 64-wide rotary queries of all heads sit in LDS) and its
 //     output O^T (512 x 32 heads, fp32) in the 256 AGPRs;
 //   * per 32-token tile: S^T[32 tok x 32 heads] = K[32 x 576] . Q^T as one
-//     chain of 36 MFMA 32x32x16, online softmax in registers (lane = head),
-//     then O^T[512 x 32] += V^T[512 x 32 tok] . P^T (32 MFMA; V^T read from
-//     the same LDS tile with transposed reads, P^T is the score registers
-//     reinterpreted: no shuffles);
+//     chain of 36 MFMA 32x32x16, online softmax in registers (lane = head), then O^T[512 x 32] += V^T[512 x 32 tok] . P^T
+//     (32 MFMA; V^T read from the same LDS tile with transposed reads, P^T is the
+//     score registers reinterpreted: no shuffles);
 //   * software pipeline: the score MFMAs of tile n, then the value MFMAs of
 //     tile n-1 with the softmax of tile n issued in pieces between them;
 //   * tiles stream global -> LDS with 16-byte direct-to-LDS loads through a ring
