@@ -124,6 +124,25 @@ def test_split_counts(splits):
     _check_decode(make(wl), splits=splits, what=f"splits={splits}")
 
 
+@pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5)])
+def test_combine_row_blocks(batch, tq, splits):
+    """The combine's row-block forms: 15 rows with 40 splits (more than the 32
+    split weights one pass holds, rows 8-14 past the eight-row pair form), 40
+    rows with 33 splits (a full 32-row block, then a block of eight rows that
+    both wave pairs share by split parity) and 9 rows with 5 splits (one row
+    past the pair form).  Against the absorbed fp64 form, which is pinned to the
+    un-absorbed oracle to 1e-12."""
+    print(f"[case] combine rows={batch * tq} splits={splits}", flush=True)
+    wl = synth.small_workload(batch=batch, tq=tq, len_lo=tq, len_hi=1500, seed=80 + splits)
+    inp = make(wl)
+    out, lse = run_decode(DevInputs(inp), splits=splits)
+    ref, ref_lse = oracle_decode(inp, form="absorbed")
+    assert_parity(bf16_to_f64(out), ref, f"rows={batch * tq} splits={splits}")
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_lse))
+    assert np.max(np.abs(got_lse - ref_lse)) <= 2e-2
+
+
 def test_max_split_count():
     """num_splits = 256 (the maximum): a 16,384-token sequence in 256 splits of
     one page each beside a 300-token one whose splits are mostly empty, Tq = 2
