@@ -83,27 +83,42 @@ const char* mla_strerror(int status);
 int mla_version(void);
 
 /*
- * q-absorption ("KV latent compression": q^T (W_uk c) = (W_uk^T q)^T c):
+ * q-absorption.  Source: "DeepSeek-V3" (llm-vis explorer), box "KV latent
+ * compression" (q^T (W_uk c) = (W_uk^T q)^T c: the key up-projection folds
+ * into the query); "Teardown: DeepSeek-V3", section 4 (W_UK of each head maps
+ * the 512-wide latent to the 128-wide content key).
  *   q_lat[m, h, j] = sum_i q_c[m, h, i] * w_uk[h, i, j]     (fp32 accumulate)
- * q_c   bf16 [M, H, d_h]   (M = B * Tq query rows)
- * w_uk  bf16 [H, d_h, d_c]
- * q_lat bf16 [M, H, d_c]   output, rounded to nearest even
- * M may be any value in [1, 65536].
+ * q_c   bf16 [M, H, d_h]   (M = B * Tq query rows), read only
+ * w_uk  bf16 [H, d_h, d_c], read only
+ * q_lat bf16 [M, H, d_c]   written, rounded to nearest even
+ * M may be any value in [1, 65536].  Errors: MLA_ERR_INVALID_ARG for NULL
+ * pointers or M outside that range, MLA_ERR_UNSUPPORTED for other dims.
  */
 int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat,
                  int M, int H, int d_h, int d_c, void* stream);
 
 /*
- * Split-KV flash decode over the paged latent cache (steps "scores", "online
- * softmax", "causal mask" and the per-split partials of the absorbed form).
- * q_lat  bf16 [B, Tq, H, d_c]   from mla_absorb_q
+ * Split-KV flash decode over the paged latent cache: scores, online softmax,
+ * causal mask and the per-split partials of the absorbed form.  Source:
+ * "Teardown: DeepSeek-V3", section 4 (score = [q_C; q_R] . [k_C; k_R] /
+ * sqrt(128 + 64), k_R shared by the heads, only c and k_R cached);
+ * "DeepSeek-V3" (llm-vis explorer), boxes "KV latent compression" (the
+ * absorbed query scores the cached latent directly) and "Scaled dot-product
+ * attention" (softmax(q k^T * scale) v with the causal mask, renormalised
+ * online block by block).
+ * q_lat  bf16 [B, Tq, H, d_c]   from mla_absorb_q, read only
  * q_r    bf16 [B, Tq, H, d_r]   rotary part of the query, already rotated
- * kv_cache, block_table, seq_lens as described above
- * softmax_scale: score scale (1/sqrt(192) for DeepSeek-V3's dims)
- * num_splits S: each sequence's ceil(L_b / block_size) blocks are cut into S
- *   contiguous ranges of ceil(blocks / S) blocks (trailing ranges may be empty)
- * part_o   fp32 [S, B, Tq, H, d_c]  out: o_s, normalised within its split
- * part_lse fp32 [S, B, Tq, H]       out: ln sum_{t in split} e^{s_t}
+ * kv_cache, block_table, seq_lens as described above (read only)
+ * softmax_scale: score scale (1/sqrt(192) for DeepSeek-V3's dims), finite > 0
+ * num_splits S in [1, MLA_MAX_SPLITS]: each sequence's ceil(L_b / block_size)
+ *   blocks are cut into S contiguous ranges of ceil(blocks / S) blocks
+ *   (trailing ranges may be empty)
+ * part_o   fp32 [S, B, Tq, H, d_c]  written: o_s, normalised within its split
+ * part_lse fp32 [S, B, Tq, H]       written: ln sum_{t in split} e^{s_t}
+ * (both may be carved from one buffer of mla_decode_workspace_bytes bytes).
+ * Errors: MLA_ERR_INVALID_ARG for NULL pointers, non-positive sizes, a
+ * non-finite or non-positive scale, S out of range, B * Tq > 65536 or
+ * Tq > max_blocks_per_seq * block_size; MLA_ERR_UNSUPPORTED for other dims.
  */
 int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
                      const uint16_t* kv_cache, const int32_t* block_table,
@@ -114,27 +129,41 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
                      float* part_o, float* part_lse, void* stream);
 
 /*
- * Log-sum-exp merge of the splits, then the W_UV up-projection.
- * part_o, part_lse as written by mla_decode_paged (M = B * Tq rows)
- * w_uv    bf16 [H, d_c, d_v]
- * out     bf16 [M, H, d_v]   out
- * lse_out fp32 [M, H] or NULL: ln sum over all splits (natural log)
- * A row whose splits are all empty gets out = 0 and lse = -inf.
+ * Log-sum-exp merge of the splits, then the W_UV up-projection.  Source:
+ * "DeepSeek-V3" (llm-vis explorer), box "Scaled dot-product attention" (the
+ * online renormalisation across key blocks, applied here across splits) and
+ * box "Output projection" (the value up-projection folds into the output
+ * side); "Teardown: DeepSeek-V3", section 4 (v_C = W_UV c).
+ * part_o, part_lse as written by mla_decode_paged for the same B, Tq and
+ *         num_splits (read only; rows of empty splits may hold anything)
+ * w_uv    bf16 [H, d_c, d_v], read only
+ * out     bf16 [B, Tq, H, d_v]   written
+ * lse_out fp32 [B, Tq, H] or NULL: ln sum over all splits (natural log)
+ * A row whose splits are all empty gets out = 0 and lse = -inf.  Errors as
+ * for mla_decode_paged (B * Tq > 65536 is MLA_ERR_INVALID_ARG).
  */
 int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv,
                 uint16_t* out, float* lse_out,
-                int M, int H, int d_c, int d_v, int num_splits, void* stream);
+                int B, int Tq, int H, int d_c, int d_v, int num_splits, void* stream);
 
 /*
- * Causal prefill in the un-absorbed form: per head, keys [W_UK c; k_R]
- * (192 wide) and values W_UV c (128 wide) are rebuilt from the cache into
- * `workspace`, then softmax(q k^T * scale) v runs with the causal mask.
+ * Causal prefill in the un-absorbed form.  Source: "Teardown: DeepSeek-V3",
+ * section 4 (k_C = W_UK c, v_C = W_UV c per head, keys [k_C; k_R] and queries
+ * [q_C; q_R] of 192 values, scale 1/sqrt(192)); "DeepSeek-V3" (llm-vis
+ * explorer), box "Scaled dot-product attention" (causal mask: position i sees
+ * positions <= i).  Per head, keys (192 wide) and values (128 wide) are
+ * rebuilt from the cache into `workspace`, then softmax(q k^T * scale) v runs
+ * with the causal mask.
  * q_c  bf16 [B, T, H, d_h], q_r bf16 [B, T, H, d_r]: queries of the LAST T
- *      positions of each sequence (positions L_b - T .. L_b - 1)
- * w_uk, w_uv as above; out bf16 [B, T, H, d_v]
- * workspace: device scratch of at least
- *      mla_prefill_workspace_bytes(B, max_blocks_per_seq, block_size, H, d_h, d_v)
- *      bytes, 256-byte aligned.
+ *      positions of each sequence (positions L_b - T .. L_b - 1), read only
+ * kv_cache, block_table, seq_lens as described above (T <= L_b), read only
+ * w_uk, w_uv as above; out bf16 [B, T, H, d_v] written
+ * workspace: caller-owned device scratch of at least
+ *      mla_prefill_workspace_bytes(B * max_blocks_per_seq * block_size, H, d_h, d_v)
+ *      bytes, 256-byte aligned; its contents on entry do not matter.
+ * Errors: MLA_ERR_INVALID_ARG for NULL pointers, non-positive sizes, a bad
+ * scale, a misaligned or too small workspace or T > max_blocks_per_seq *
+ * block_size; MLA_ERR_UNSUPPORTED for other dims.
  */
 int mla_prefill(const uint16_t* q_c, const uint16_t* q_r,
                 const uint16_t* kv_cache, const int32_t* block_table,
@@ -218,13 +247,22 @@ int mla_output_project(const uint16_t* o, const uint16_t* w_o, uint16_t* y,
                        int M, int d_in, int d_out, void* stream);
 size_t mla_output_project_workspace_bytes(int M, int d_in, int d_out);
 
-/* Bytes of part_o plus part_lse for one decode step (two separate buffers). */
+/*
+ * Workspace of one decode step: part_o then part_lse in one buffer, part_lse
+ * starting at mla_decode_part_o_bytes(...) rounded up to 256 bytes.  Returns
+ * the total (0 on non-positive arguments).
+ */
+size_t mla_decode_workspace_bytes(int B, int Tq, int H, int d_c, int num_splits);
+/* Bytes of part_o and of part_lse alone (0 on non-positive arguments). */
 size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits);
 size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits);
 
-/* Workspace bytes mla_prefill needs. */
-size_t mla_prefill_workspace_bytes(int B, int max_blocks_per_seq, int block_size,
-                                   int H, int d_h, int d_v);
+/*
+ * Workspace bytes mla_prefill needs: rebuilt bf16 content keys and values of
+ * every cache slot the block table can address, total_kv_tokens =
+ * B * max_blocks_per_seq * block_size (0 on non-positive arguments).
+ */
+size_t mla_prefill_workspace_bytes(long total_kv_tokens, int H, int d_h, int d_v);
 
 /*
  * Suggested num_splits for a decode step: enough work-groups (one per

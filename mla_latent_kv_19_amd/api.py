@@ -12,6 +12,7 @@ bf16 tensors are torch.bfloat16 (bit-identical to the ABI's uint16 patterns).
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -25,11 +26,76 @@ H, D_C, D_R, D_H, D_V, BLOCK = 128, 512, 64, 128, 128, 64
 
 EXPORTED = (
     "mla_strerror", "mla_version", "mla_absorb_q", "mla_decode_paged", "mla_combine",
-    "mla_prefill", "mla_decode_part_o_bytes", "mla_decode_part_lse_bytes",
+    "mla_prefill", "mla_decode_workspace_bytes", "mla_decode_part_o_bytes",
+    "mla_decode_part_lse_bytes",
     "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
     "mla_cache_append_workspace_bytes", "mla_query_project", "mla_query_project_workspace_bytes",
     "mla_output_project", "mla_output_project_workspace_bytes", "mla_hbm_read_probe",
 )
+
+
+# Debug mode: host checks of the device-resident metadata (block table and
+# sequence lengths) before each call that reads it.  They copy the metadata to
+# the host, a synchronisation, so they are off unless MLA_DEBUG is set (or
+# set_debug(True) is called).
+_debug = os.environ.get("MLA_DEBUG", "0") not in ("", "0")
+
+
+def set_debug(on):
+    """Turn the host-side metadata checks on or off; returns the previous setting."""
+    global _debug
+    prev, _debug = _debug, bool(on)
+    return prev
+
+
+def debug_enabled():
+    return _debug
+
+
+def check_paged_metadata(block_table, seq_lens, num_blocks, n_query, block_size=BLOCK):
+    """Host check of the preconditions the library documents but cannot check
+    without a synchronisation ("Teardown: DeepSeek-V3", section 12: the latent
+    cache of one tenant must stay isolated from another's):
+
+    * n_query <= L_b <= max_blocks * block_size for every sequence b
+      (n_query = Tq in decode, T in prefill: the query tokens are cached);
+    * 0 <= block_table[b, p] < num_blocks for every page p < ceil(L_b / block_size)
+      a sequence uses;
+    * no physical block is used twice (by two sequences, or twice by one).
+
+    Accepts numpy arrays or torch tensors on any device (device tensors are
+    copied to the host).  Raises ValueError naming the first violation.
+    """
+    def host(a):
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+        return np.asarray(a)
+
+    table = host(block_table)
+    lens = host(seq_lens)
+    if table.ndim != 2 or lens.ndim != 1 or table.shape[0] != lens.shape[0]:
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    cap = table.shape[1] * block_size
+    bad = np.nonzero((lens < n_query) | (lens > cap))[0]
+    if bad.size:
+        b = int(bad[0])
+        raise ValueError(f"sequence {b}: seq_len {int(lens[b])} outside [{n_query}, {cap}] "
+                         f"(query tokens .. max_blocks_per_seq * block_size)")
+    pages = (lens.astype(np.int64) + block_size - 1) // block_size
+    used = np.arange(table.shape[1])[None, :] < pages[:, None]
+    ids = table.astype(np.int64)[used]
+    owner = np.nonzero(used)[0]
+    out = np.nonzero((ids < 0) | (ids >= num_blocks))[0]
+    if out.size:
+        k = int(out[0])
+        raise ValueError(f"sequence {int(owner[k])}: block id {int(ids[k])} of a used page "
+                         f"outside [0, {num_blocks})")
+    uniq, first, counts = np.unique(ids, return_index=True, return_counts=True)
+    if np.any(counts > 1):
+        blk = int(uniq[np.argmax(counts > 1)])
+        seqs = sorted({int(o) for o in owner[ids == blk]})
+        raise ValueError(f"block {blk} is used more than once (sequences {seqs}): "
+                         f"a page may belong to one sequence position only")
 
 
 class MLAError(RuntimeError):
@@ -58,13 +124,15 @@ def load():
     lib.mla_version.argtypes, lib.mla_version.restype = [], I
     lib.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, P]
     lib.mla_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, P]
-    lib.mla_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.mla_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_prefill.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, I, F, P]
     for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill"):
         getattr(lib, fn).restype = I
+    lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.mla_decode_workspace_bytes.restype = Z
     lib.mla_decode_part_o_bytes.argtypes, lib.mla_decode_part_o_bytes.restype = [I, I, I, I, I], Z
     lib.mla_decode_part_lse_bytes.argtypes, lib.mla_decode_part_lse_bytes.restype = [I, I, I, I], Z
-    lib.mla_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.mla_prefill_workspace_bytes.argtypes = [ctypes.c_long, I, I, I]
     lib.mla_prefill_workspace_bytes.restype = Z
     lib.mla_decode_num_splits.argtypes, lib.mla_decode_num_splits.restype = [I, I, I, I, I, I], I
     lib.mla_cache_append.argtypes = [P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, F, F, P]
@@ -182,6 +250,8 @@ def decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, softmax_scale, spl
     _need(part_o, "part_o", torch.float32, (splits, b, tq, H, D_C))
     _need(part_lse, "part_lse", torch.float32, (splits, b, tq, H))
     dev = _same_device(q_lat, q_r, kv_cache, block_table, seq_lens, part_o, part_lse)
+    if _debug:
+        check_paged_metadata(block_table, seq_lens, kv_cache.shape[0], tq)
     _check("mla_decode_paged", load().mla_decode_paged(
         _ptr(q_lat), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
         b, tq, H, D_C, D_R, kv_cache.shape[0], BLOCK, block_table.shape[1],
@@ -205,7 +275,7 @@ def combine(part_o, part_lse, w_uv, out=None, lse_out=None, want_lse=False):
     dev = _same_device(part_o, part_lse, w_uv, out, lse_out)
     _check("mla_combine", load().mla_combine(
         _ptr(part_o), _ptr(part_lse), _ptr(w_uv), _ptr(out), _ptr(lse_out),
-        b * tq, H, D_C, D_V, s, _stream(dev)))
+        b, tq, H, D_C, D_V, s, _stream(dev)))
     return (out, lse_out) if lse_out is not None else out
 
 
@@ -235,7 +305,26 @@ def decode_step(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_s
 
 
 def prefill_workspace_bytes(batch, max_blocks_per_seq):
-    return load().mla_prefill_workspace_bytes(batch, max_blocks_per_seq, BLOCK, H, D_H, D_V)
+    return load().mla_prefill_workspace_bytes(batch * max_blocks_per_seq * BLOCK, H, D_H, D_V)
+
+
+def decode_workspace_bytes(batch, tq, splits):
+    """Bytes of one buffer holding part_o then part_lse (see decode_workspace)."""
+    return load().mla_decode_workspace_bytes(batch, tq, H, D_C, splits)
+
+
+def decode_workspace(batch, tq, splits, device=None):
+    """(part_o [S,B,Tq,H,512], part_lse [S,B,Tq,H]) fp32 views of one device
+    buffer laid out as mla_decode_workspace_bytes describes."""
+    nbytes = decode_workspace_bytes(batch, tq, splits)
+    if nbytes <= 0:
+        raise ValueError("invalid decode workspace shape")
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=device or "cuda")
+    n_o = splits * batch * tq * H * D_C
+    off = (n_o * 4 + 255) // 256 * 64
+    part_o = buf[:n_o].view(splits, batch, tq, H, D_C)
+    part_lse = buf[off:off + splits * batch * tq * H].view(splits, batch, tq, H)
+    return part_o, part_lse
 
 
 def prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale,
@@ -258,6 +347,8 @@ def prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale
     if workspace.numel() < nbytes:
         raise ValueError(f"prefill workspace needs {nbytes} bytes")
     dev = _same_device(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, out, workspace)
+    if _debug:
+        check_paged_metadata(block_table, seq_lens, kv_cache.shape[0], t)
     _check("mla_prefill", load().mla_prefill(
         _ptr(q_c), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
         _ptr(w_uk), _ptr(w_uv), _ptr(out), _ptr(workspace), workspace.numel(),

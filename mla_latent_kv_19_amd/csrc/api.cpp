@@ -107,19 +107,30 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t*
     return MLA_ERR_INVALID_ARG;
   if (H != kH || d_c != kDC || d_r != kDR || block_size != kBlock || Tq > kMaxTq)
     return MLA_ERR_UNSUPPORTED;
+  if ((long)Tq > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
   return status_of(mla_launch_decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq,
                                            max_blocks_per_seq, softmax_scale, num_splits, part_o,
                                            part_lse, static_cast<hipStream_t>(stream)));
 }
 
 int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv, uint16_t* out,
-                float* lse_out, int M, int H, int d_c, int d_v, int num_splits, void* stream) {
-  if (!part_o || !part_lse || !w_uv || !out || M <= 0 || H <= 0 || d_c <= 0 || d_v <= 0 ||
-      num_splits < 1 || num_splits > MLA_MAX_SPLITS || M > kMaxRows)
+                float* lse_out, int B, int Tq, int H, int d_c, int d_v, int num_splits,
+                void* stream) {
+  if (!part_o || !part_lse || !w_uv || !out || B <= 0 || Tq <= 0 || H <= 0 || d_c <= 0 ||
+      d_v <= 0 || num_splits < 1 || num_splits > MLA_MAX_SPLITS || (long)B * Tq > kMaxRows)
     return MLA_ERR_INVALID_ARG;
   if (H != kH || d_c != kDC || d_v != kDV) return MLA_ERR_UNSUPPORTED;
-  return status_of(mla_launch_combine(part_o, part_lse, w_uv, out, lse_out, M, num_splits,
+  // The partial rows [S, B, Tq, H, d_c] are (split, query row) pairs: the
+  // merge and the up-projection see the B * Tq query rows alike.
+  return status_of(mla_launch_combine(part_o, part_lse, w_uv, out, lse_out, B * Tq, num_splits,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_workspace_bytes(int B, int Tq, int H, int d_c, int num_splits) {
+  const size_t o = mla_decode_part_o_bytes(B, Tq, H, d_c, num_splits);
+  const size_t l = mla_decode_part_lse_bytes(B, Tq, H, num_splits);
+  if (o == 0 || l == 0) return 0;
+  return (o + 255) / 256 * 256 + l;
 }
 
 size_t mla_decode_part_o_bytes(int B, int Tq, int H, int d_c, int num_splits) {
@@ -132,12 +143,11 @@ size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits) {
   return (size_t)num_splits * B * Tq * H * sizeof(float);
 }
 
-size_t mla_prefill_workspace_bytes(int B, int max_blocks_per_seq, int block_size, int H, int d_h,
-                                   int d_v) {
-  if (B <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 || H <= 0 || d_h <= 0 || d_v <= 0)
-    return 0;
-  // Rebuilt content keys and values for every cached position: bf16 [B, H, Lmax, d_h + d_v].
-  return (size_t)B * max_blocks_per_seq * block_size * H * (d_h + d_v) * 2;
+size_t mla_prefill_workspace_bytes(long total_kv_tokens, int H, int d_h, int d_v) {
+  if (total_kv_tokens <= 0 || H <= 0 || d_h <= 0 || d_v <= 0) return 0;
+  // Rebuilt content keys and values for every addressable cache slot:
+  // bf16 [B, H, max_blocks * block_size, d_h + d_v].
+  return (size_t)total_kv_tokens * H * (d_h + d_v) * 2;
 }
 
 int mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv_cache,
@@ -155,7 +165,8 @@ int mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* kv_cac
   if (H != kH || d_c != kDC || d_r != kDR || d_h != kDH || d_v != kDV || block_size != kBlock)
     return MLA_ERR_UNSUPPORTED;
   if ((long)T > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
-  if (workspace_bytes < mla_prefill_workspace_bytes(B, max_blocks_per_seq, block_size, H, d_h, d_v))
+  if (workspace_bytes <
+      mla_prefill_workspace_bytes((long)B * max_blocks_per_seq * block_size, H, d_h, d_v))
     return MLA_ERR_INVALID_ARG;
   return status_of(mla_launch_prefill(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, out,
                                       workspace, B, T, max_blocks_per_seq, softmax_scale,

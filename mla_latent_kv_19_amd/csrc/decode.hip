@@ -152,7 +152,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     voff = (lane >> 3) * kRowBytes + ((lane & 7) ^ f) * 16;
   }
 
-  const int L = seq_lens[b];
+  // seq_lens is caller metadata that is not validated on the host: clamp it
+  // into [Tq, max_blocks * 64] so that no block-table read leaves the row.
+  const int L = min(max(seq_lens[b], Tq), max_blocks * kTok);
   const int n_pages = (L + kTok - 1) / kTok;
   const int per = (n_pages + num_splits - 1) / num_splits;
   const int p0 = min(n_pages, split * per);
@@ -252,25 +254,29 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     lds_u8* stage;       // its LDS destination
   };
   auto top = [&](int n, Next& nx) {
-    // Tile n has landed for every wave, every wave is done with tile n-2, whose
-    // stage then takes tile n+2.
+    // This wave's rows of tile n have landed (its own direct-to-LDS loads).
     if (n + 1 < ntiles) wait_vmcnt<kLoadsPerThread>(); else wait_vmcnt<0>();
+    const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
+    if (valid < 8 * wave + 8) {
+      // Rows past the sequence end may hold anything (NaN): each wave zeroes
+      // the ones of its own row group (its loads of them are complete) so
+      // that 0-weight tokens contribute exactly 0 to the value product; the
+      // barrier below publishes the zeroes before any wave reads the tile.
+      // Nobody reads this stage's previous tile any more: its value product
+      // ended before the barrier of iteration n - 2.
+      lds_u8* stage = smem + (n % kRing) * kTileBytes;
+      for (int idx = lane; idx < 8 * kChunks; idx += 64) {
+        const int t = 8 * wave + idx / kChunks;
+        if (t >= valid) st_lds_zero16(stage + tile_off(t, idx % kChunks));
+      }
+    }
+    // Tile n is complete for every wave, every wave is done with tile n-2,
+    // whose stage then takes tile n+2.
     lds_barrier();
     nx.g = nullptr;
     if (n + 2 < ntiles) {
       nx.g = reinterpret_cast<const char*>(tile_rows(n + 2)) + wave * 8 * kRowBytes;
       nx.stage = smem + ((n + 2) % kRing) * kTileBytes + wave * kRowGrpBytes;
-    }
-    const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
-    if (valid < kTileTok) {
-      // Rows past the sequence end may hold anything (NaN): zero them so that
-      // 0-weight tokens contribute exactly 0 to the value product.  They are
-      // read by the value product one barrier later.
-      lds_u8* stage = smem + (n % kRing) * kTileBytes;
-      for (int idx = tid; idx < (kTileTok - valid) * kChunks; idx += kDecThreads) {
-        const int t = valid + idx / kChunks;
-        st_lds_zero16(stage + tile_off(t, idx % kChunks));
-      }
     }
   };
 

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kv_kernel(
   const int tblk = blockIdx.x % n_tblk;
   const int h = (blockIdx.x / n_tblk) % 128;
   const int b = blockIdx.x / (n_tblk * 128);
-  const int L = seq_lens[b];
+  // Unvalidated caller metadata: keep every block-table read inside the row.
+  const int L = min(seq_lens[b], max_blocks * 64);
   const int t0 = tblk * kPfPos;
   if (t0 >= L) return;
   const int Lpad = max_blocks * 64;
@@ -318,7 +319,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(
   const int qblk = n_qblk - 1 - (int)(blockIdx.x / per_q);
   const int bh = blockIdx.x % per_q;
   const int b = bh / 128, h = bh % 128;
-  const int L = seq_lens[b];
+  // Unvalidated caller metadata: clamp into [T, max_blocks * 64] (T fits: the
+  // host checks it) so that no key index leaves the workspace or the table row.
+  const int L = min(max(seq_lens[b], T), max_blocks * 64);
   const int Lpad = max_blocks * 64;
 
   const int tid = threadIdx.x;

@@ -17,9 +17,12 @@ Sources, by page title:
 
 Readings where the pages are silent:
 
-* RMSNorm is x / sqrt(mean(x^2) + eps) * gamma over the 512 latent values,
-  with a learned gain gamma; the pages name the module but give neither the
-  formula nor eps, so eps is an argument.
+* Same page, box "RMSNorm": y = x / sqrt(mean(x^2) + eps) * g with a learned
+  per-feature gain g and eps = 0.000001, the reduction done in fp32 in bf16
+  models.  The box describes the 7168-wide norms; kv_norm = RMSNorm(512) is
+  the same module over the 512 latent values, so the same formula and eps
+  apply.  Here the reduction is exact (float64), eps defaults to the printed
+  value and stays an argument.
 * The pages mention a YaRN x40 frequency remap without defining it; it is
   not applied here (plain RoPE as printed).
 * Angles are computed exactly (float64) rather than in the framework's
@@ -30,25 +33,30 @@ All arithmetic is float64 on the exact values handed in.  Nothing here rounds.
 
 import numpy as np
 
+# eps of the explorer's "RMSNorm" box (printed as 0.000001).
+RMS_EPS = 1e-6
+# theta of the explorer's "Rotary position embedding (RoPE)" box.
+ROPE_THETA = 10000.0
+
 
 def kv_down(x, w_kv):
     """[M, d_model] x [d_c + d_r, d_model] (a linear layer's weight) -> [M, d_c + d_r]."""
     return np.asarray(x, dtype=np.float64) @ np.asarray(w_kv, dtype=np.float64).T
 
 
-def rms_norm(c, gamma, eps):
-    """RMSNorm over the last axis: c / sqrt(mean(c^2) + eps) * gamma."""
+def rms_norm(c, gamma, eps=RMS_EPS):
+    """RMSNorm over the last axis: c / sqrt(mean(c^2) + eps) * gamma ("RMSNorm" box)."""
     c = np.asarray(c, dtype=np.float64)
     rms = np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
     return c / rms * np.asarray(gamma, dtype=np.float64)
 
 
-def rope_inv_freq(d_r, theta):
+def rope_inv_freq(d_r, theta=ROPE_THETA):
     """1 / theta^(2i / d_r) for i = 0 .. d_r/2 - 1."""
     return 1.0 / (float(theta) ** (np.arange(0, d_r, 2, dtype=np.float64) / d_r))
 
 
-def apply_rope(k, pos, theta):
+def apply_rope(k, pos, theta=ROPE_THETA):
     """Rotate consecutive pairs of the last axis of k ([..., d_r]) by pos * inv_freq.
 
     ``pos`` broadcasts against the leading axes of k.
@@ -63,7 +71,7 @@ def apply_rope(k, pos, theta):
     return out
 
 
-def cache_rows(x, w_kv, gamma, positions, eps, theta, d_c=512):
+def cache_rows(x, w_kv, gamma, positions, eps=RMS_EPS, theta=ROPE_THETA, d_c=512):
     """The cache rows [M, d_c + d_r] of M new tokens: RMSNorm(latent) | RoPE(key)."""
     y = kv_down(x, w_kv)
     c = rms_norm(y[:, :d_c], gamma, eps)
@@ -71,8 +79,8 @@ def cache_rows(x, w_kv, gamma, positions, eps, theta, d_c=512):
     return np.concatenate([c, k_r], axis=1)
 
 
-def cache_append(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache, eps, theta,
-                 d_c=512):
+def cache_append(x, w_kv, gamma, seq_idx, positions, block_table, kv_cache, eps=RMS_EPS,
+                 theta=ROPE_THETA, d_c=512):
     """Write the rows of M new tokens into a copy of the paged cache.
 
     Token m belongs to sequence seq_idx[m] at position positions[m]; its row

@@ -15,30 +15,24 @@ Sources, by page title:
 
 Readings where the pages are silent: the per-head 192 outputs of W_UQ are the
 content part (128) then the rotary part (64), the order of [q_C; q_R];
-RMSNorm and RoPE as in ``oracle.cache_append`` (eps an argument, no YaRN
-remap, exact angles).
+RMSNorm and RoPE as in ``oracle.cache_append`` (the explorer's RMSNorm box
+with eps = 1e-6, no YaRN remap, exact angles).
 
-All arithmetic is float64 on the exact values handed in.  Nothing here rounds,
-except where a function says it models an intermediate the pages store.
+All arithmetic is float64 on the exact values handed in.  Nothing here rounds.
 """
 
 import numpy as np
 
-from .cache_append import apply_rope, rms_norm
+from .cache_append import RMS_EPS, ROPE_THETA, apply_rope, rms_norm
 
 
-def query_project(x, w_dq, gamma_q, w_uq, positions, eps, theta, n_heads=128, d_h=128, d_r=64,
-                  round_cq=None):
-    """(q_c [M, H, d_h], q_r [M, H, d_r]) of M tokens.
-
-    ``round_cq``, if given, is applied to the normalised c_q before the second
-    product (a kernel that stores c_q in bf16 is compared with
-    round_cq = bf16 rounding; the default keeps it exact).
-    """
+def query_project(x, w_dq, gamma_q, w_uq, positions, eps=RMS_EPS, theta=ROPE_THETA, n_heads=128,
+                  d_h=128, d_r=64):
+    """(q_c [M, H, d_h], q_r [M, H, d_r]) of M tokens: c_q = W_DQ x, RMSNorm with
+    gain gamma_q, q = W_UQ c_q split per head into [q_C; q_R'], q_R' rotated at
+    the token's position."""
     c_q = np.asarray(x, dtype=np.float64) @ np.asarray(w_dq, dtype=np.float64).T
     c_q = rms_norm(c_q, gamma_q, eps)
-    if round_cq is not None:
-        c_q = round_cq(c_q)
     q = (c_q @ np.asarray(w_uq, dtype=np.float64).T).reshape(len(c_q), n_heads, d_h + d_r)
     q_c = q[..., :d_h]
     q_r = apply_rope(q[..., d_h:], np.asarray(positions)[:, None], theta)

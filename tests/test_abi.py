@@ -85,22 +85,26 @@ def test_decode_argument_errors():
     assert _decode(lib, block_size=16) == U
     assert _decode(lib, Tq=9) == U
     assert _decode(lib, d_r=32) == U
+    assert _decode(lib, B=40000, Tq=2) == E                   # more than 65,536 query rows
 
 
 def test_combine_argument_errors():
     lib = _lib()
     E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
-    assert lib.mla_combine(NULL, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 128, 2, NULL) == E
-    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 128, 0, NULL) == E
-    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 128, 512, 64, 2, NULL) == U
+    assert lib.mla_combine(NULL, FAKE, FAKE, FAKE, NULL, 4, 1, 128, 512, 128, 2, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 1, 128, 512, 128, 0, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 0, 128, 512, 128, 2, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 40000, 2, 128, 512, 128, 2, NULL) == E
+    assert lib.mla_combine(FAKE, FAKE, FAKE, FAKE, NULL, 4, 1, 128, 512, 64, 2, NULL) == U
 
 
 def test_prefill_argument_errors():
     lib = _lib()
     E, U = api.MLA_ERR_INVALID_ARG, api.MLA_ERR_UNSUPPORTED
     aligned = ctypes.c_void_p(0x10000)
-    need = lib.mla_prefill_workspace_bytes(1, 64, 64, 128, 128, 128)
+    need = lib.mla_prefill_workspace_bytes(1 * 64 * 64, 128, 128, 128)
     assert need == 64 * 64 * 128 * 256 * 2
+    assert lib.mla_prefill_workspace_bytes(0, 128, 128, 128) == 0
 
     def call(ws=aligned, ws_bytes=need, T=4096, H=128, max_blocks=64):
         return lib.mla_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
@@ -118,6 +122,10 @@ def test_workspace_sizes_and_split_heuristic():
     assert lib.mla_decode_part_o_bytes(64, 1, 128, 512, 4) == 4 * 64 * 128 * 512 * 4
     assert lib.mla_decode_part_lse_bytes(64, 1, 128, 4) == 4 * 64 * 128 * 4
     assert lib.mla_decode_part_o_bytes(0, 1, 128, 512, 4) == 0
+    # One buffer: part_o, then part_lse at a 256-byte boundary.
+    assert lib.mla_decode_workspace_bytes(64, 1, 128, 512, 4) == 4 * 64 * 128 * 513 * 4
+    assert lib.mla_decode_workspace_bytes(1, 1, 128, 512, 1) == 128 * 512 * 4 + 128 * 4
+    assert lib.mla_decode_workspace_bytes(0, 1, 128, 512, 1) == 0
     # 64 sequences on 256 compute units: 4 splits; 8 long sequences: 32 splits.
     assert lib.mla_decode_num_splits(64, 1, 128, 32768, 64, 256) == 4
     assert lib.mla_decode_num_splits(8, 1, 128, 163840, 64, 256) == 32

@@ -228,19 +228,57 @@ def test_workload_batched_full():
     assert_parity(got, ref_u, "batched (un-absorbed sample)")
 
 
-def _sampled_full_size(name, extra_heads=(0, 127)):
+def _distinct_picks(lens, n=3):
+    """Shortest, longest and a middle sequence; when lengths tie, the first,
+    last and middle sequence (n distinct sequences, n <= 3, whenever B >= n)."""
+    B = len(lens)
+    picks = []
+    for b in (int(np.argmin(lens)), int(np.argmax(lens)), 0, B - 1, B // 2):
+        if b not in picks:
+            picks.append(b)
+        if len(picks) == min(n, B):
+            break
+    return sorted(picks)
+
+
+SAMPLED_HEADS = [0, 1, 64, 127]
+
+
+def _sampled_full_size(name, n_picks=3):
+    """A full-size workload in the launch configuration the benchmark times
+    (the library's split heuristic), against the fp64 oracle on:
+      * every sequence x heads 0, 1, 64 and 127 (absorbed form, itself pinned
+        to the un-absorbed definition to 1e-12), outputs and log-sum-exps;
+      * n_picks distinct sequences x all 128 heads (absorbed form);
+      * the shortest and the longest of those (first and last when lengths
+        tie) x heads 0 and 127 in the un-absorbed form (the definition);
+    and every output finite."""
     inp = make(synth.WORKLOADS[name])
     dev = DevInputs(inp)
     out, lse = run_decode(dev)
-    lens = inp.seq_lens
-    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), len(lens) // 2})
-    ref, ref_lse = oracle_decode(inp, batches=seqs, form="absorbed")
-    got = bf16_to_f64(out)[seqs]
-    assert_parity(got, ref, f"{name} (sequences {seqs}, all heads)")
-    assert np.max(np.abs(lse.cpu().numpy()[seqs] - ref_lse)) <= 2e-2
-    ref_u, _ = oracle_decode(inp, batches=seqs[:1], heads=list(extra_heads))
-    assert_parity(got[:1][:, :, list(extra_heads)], ref_u, f"{name} (un-absorbed sample)")
-    assert np.all(np.isfinite(bf16_to_f64(out)))
+    got_all = bf16_to_f64(out)
+    lse_all = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_all)) and np.all(np.isfinite(lse_all))
+    B = inp.wl.batch
+    ref, ref_lse = oracle_decode(inp, heads=SAMPLED_HEADS, form="absorbed")
+    assert_parity(got_all[:, :, SAMPLED_HEADS], ref,
+                  f"{name} (all {B} sequences, heads {SAMPLED_HEADS})")
+    assert np.max(np.abs(lse_all[:, :, SAMPLED_HEADS] - ref_lse)) <= 2e-2
+    picks = _distinct_picks(inp.seq_lens, n_picks)
+    ref, ref_lse = oracle_decode(inp, batches=picks, form="absorbed")
+    assert_parity(got_all[picks], ref, f"{name} (sequences {picks}, all heads)")
+    assert np.max(np.abs(lse_all[picks] - ref_lse)) <= 2e-2
+    ends = [picks[0], picks[-1]]
+    ref_u, _ = oracle_decode(inp, batches=ends, heads=[0, 127])
+    assert_parity(got_all[ends][:, :, [0, 127]], ref_u,
+                  f"{name} (un-absorbed, sequences {ends}, heads 0 and 127)")
+
+
+def test_distinct_picks():
+    assert _distinct_picks(np.array([5, 5, 5, 5])) == [0, 2, 3]
+    assert _distinct_picks(np.array([5, 5, 5, 5]), 2) == [0, 3]
+    assert _distinct_picks(np.array([9, 1, 4, 7, 3])) == [0, 1, 4]
+    assert _distinct_picks(np.array([3, 3])) == [0, 1]
 
 
 def test_workload_mtp_sampled():
@@ -250,7 +288,7 @@ def test_workload_mtp_sampled():
 
 def test_workload_long_sampled():
     print("[case] workload long", flush=True)
-    _sampled_full_size("long")
+    _sampled_full_size("long", n_picks=2)
 
 
 def test_workload_headline_sampled():
@@ -309,3 +347,29 @@ def test_max_rows():
     assert_parity(bf16_to_f64(out[idx]), ref, "max rows (sampled sequences)")
     got_lse = lse[idx].cpu().numpy().astype(np.float64)
     assert np.max(np.abs(got_lse - ref_lse)) <= 2e-2
+
+
+def test_debug_mode_rejects_bad_metadata():
+    """With the binding's debug checks on, a valid call runs as before and a
+    block shared by two sequences or a length past the table row is rejected
+    on the host, before any kernel is launched."""
+    print("[case] debug metadata checks", flush=True)
+    wl = synth.small_workload(batch=3, tq=2, len_lo=2, len_hi=300, seed=151)
+    inp = make(wl, seq_lens=[130, 64, 200])
+    dev = DevInputs(inp)
+    prev = api.set_debug(True)
+    try:
+        out, _ = run_decode(dev, splits=2)
+        assert bool(torch.isfinite(out).all())
+        shared = dev.table.clone()
+        shared[1, 0] = shared[0, 1]
+        with pytest.raises(ValueError, match="used more than once"):
+            api.decode_step(dev.q_c, dev.q_r, dev.kv, shared, dev.lens, dev.w_uk, dev.w_uv,
+                            wl.scale, splits=2)
+        long_lens = dev.lens.clone()
+        long_lens[2] = dev.table.shape[1] * 64 + 1
+        with pytest.raises(ValueError, match="sequence 2"):
+            api.decode_step(dev.q_c, dev.q_r, dev.kv, dev.table, long_lens, dev.w_uk, dev.w_uv,
+                            wl.scale, splits=2)
+    finally:
+        api.set_debug(prev)

@@ -156,3 +156,33 @@ def test_output_project_against_brute_force():
     for m in range(2):
         for d in range(3):
             assert got[m, d] == pytest.approx(sum(o[m, j] * w_o[d, j] for j in range(6)), rel=1e-13)
+
+
+def test_printed_rmsnorm_eps_and_rope_theta():
+    """The oracle's and the binding's defaults are the values the pages print:
+    eps of the explorer's "RMSNorm" box and theta of its RoPE box
+    (tests/golden/page_facts.json)."""
+    import inspect
+    import json
+    import os
+
+    from oracle import projections as pj
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")) as f:
+        facts = json.load(f)
+    eps, theta = facts["rmsnorm_eps"]["value"], facts["rope_theta"]["value"]
+    assert float(facts["rmsnorm_eps"]["printed"]) == eps
+    assert ca.RMS_EPS == eps and ca.ROPE_THETA == theta
+    for fn in (ca.rms_norm, ca.cache_rows, ca.cache_append, pj.query_project):
+        params = inspect.signature(fn).parameters
+        assert params["eps"].default == eps, fn.__name__
+    for fn in (ca.rope_inv_freq, ca.apply_rope, ca.cache_rows, ca.cache_append, pj.query_project):
+        assert inspect.signature(fn).parameters["theta"].default == theta, fn.__name__
+    # The binding's defaults (read from its source: importing it needs torch only).
+    from mla_latent_kv_19_amd import api
+    for fn in (api.cache_append, api.query_project):
+        params = inspect.signature(fn).parameters
+        assert params["eps"].default == eps and params["rope_theta"].default == theta, fn.__name__
+    # The printed formula with eps: a vector of mean square 1e-6 is scaled by 1/sqrt(2e-6).
+    x = np.full(512, 1e-3)
+    np.testing.assert_allclose(ca.rms_norm(x, np.ones(512)), x / math.sqrt(2e-6), rtol=1e-14)

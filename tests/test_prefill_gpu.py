@@ -93,9 +93,22 @@ def test_prefill_rows_match_decode():
         assert np.linalg.norm(d - got[:, t]) <= 1e-2 * np.linalg.norm(got[:, t])
 
 
+# Queries of the T = 4096 workload compared on all 128 heads: the first and
+# last of the sequence, both sides of every boundary of the kernels' 32-query
+# waves, 64-key tiles and 256-query blocks at several depths, and a seeded
+# sample of the rest.
+def _prefill_query_sample(T, n_random=16, seed=5):
+    fixed = {0, 1, 31, 32, 63, 64, 65, 127, 128, 255, 256, 257, 511, 512, 1023, 1024,
+             2047, 2048, 3071, 3072, 4031, 4032, 4063, 4064, 4094, 4095}
+    rng = np.random.default_rng(seed)
+    rand = set(int(t) for t in rng.choice(T, size=n_random, replace=False))
+    return sorted(t for t in fixed | rand if t < T)
+
+
 def test_workload_prefill_sampled():
-    """T = L = 4096, B = 1: every query of heads 0, 1, 64 and 127 against the
-    un-absorbed oracle; all outputs finite."""
+    """T = L = 4096, B = 1, against the un-absorbed fp64 oracle: every query of
+    heads 0, 1, 64 and 127, and all 128 heads for at least 32 queries spread
+    over the causal range; all outputs finite."""
     print("[case] workload prefill", flush=True)
     inp = make(synth.WORKLOADS["prefill"])
     got = _run_prefill(DevInputs(inp))
@@ -103,3 +116,13 @@ def test_workload_prefill_sampled():
     heads = [0, 1, 64, 127]
     ref = _oracle_prefill(inp, heads=heads)
     assert_parity(got[:, :, heads], ref, "prefill T=4096 (4 heads, all queries)")
+    T = inp.wl.tq
+    qs = _prefill_query_sample(T)
+    assert len(qs) >= 32
+    rows = oracle.gather_rows(inp.values("kv_cache"), inp.block_table[0], int(inp.seq_lens[0]))
+    L = int(inp.seq_lens[0])
+    ref_q, _ = oracle.attend_unabsorbed(inp.values("q_c")[0, qs], inp.values("q_r")[0, qs],
+                                        rows[:, :512], rows[:, 512:], inp.values("w_uk"),
+                                        inp.values("w_uv"), inp.wl.scale,
+                                        [L - T + t + 1 for t in qs])
+    assert_parity(got[0, qs], ref_q, f"prefill T=4096 (all heads, {len(qs)} queries)")
