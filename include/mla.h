@@ -70,11 +70,16 @@ enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = 1,
   MLA_ERR_UNSUPPORTED = 2,
-  MLA_ERR_HIP = 3
+  MLA_ERR_HIP = 3,
+  MLA_ERR_NOALLOC_LIMIT = 4
 };
 
 /* Largest num_splits accepted by mla_decode_paged / mla_combine. */
 #define MLA_MAX_SPLITS 256
+
+/* Most (split, query row) pairs, num_splits * B * Tq, that mla_decode_noalloc
+ * keeps in its library-owned buffer (64 MiB + 128 KiB per GPU). */
+#define MLA_NOALLOC_MAX_PAIRS 256
 
 /* Static string describing a status code (never NULL). */
 const char* mla_strerror(int status);
@@ -145,6 +150,30 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
 int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv,
                 uint16_t* out, float* lse_out,
                 int B, int Tq, int H, int d_c, int d_v, int num_splits, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * mla_decode_paged followed by one mla_combine (same kernels, same results
+ * bit for bit), with part_o and part_lse kept in a buffer the library owns
+ * instead of caller workspace.  Allocates nothing: the buffer is a static
+ * device array of MLA_NOALLOC_MAX_PAIRS (split, query row) pairs, 64 MiB +
+ * 128 KiB, one per GPU the library runs on, held until the process ends; its
+ * device address is looked up once per device on the first call there.
+ * Arguments as for mla_decode_paged and mla_combine (out bf16 [B, Tq, H, d_v],
+ * lse_out fp32 [B, Tq, H] or NULL).  Every call on one GPU shares that GPU's
+ * buffer: calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race and must not be issued.  Errors as for those two
+ * entry points, plus MLA_ERR_NOALLOC_LIMIT when num_splits * B * Tq exceeds
+ * MLA_NOALLOC_MAX_PAIRS.
+ */
+int mla_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_r,
+                       const uint16_t* kv_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, const uint16_t* w_uv,
+                       uint16_t* out, float* lse_out,
+                       int B, int Tq, int H, int d_c, int d_r, int d_v,
+                       int num_blocks, int block_size, int max_blocks_per_seq,
+                       float softmax_scale, int num_splits, void* stream);
 
 /*
  * Causal prefill in the un-absorbed form.  Source: "Teardown: DeepSeek-V3",

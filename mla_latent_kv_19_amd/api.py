@@ -19,7 +19,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so"
 _lib = None
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
+MLA_ERR_NOALLOC_LIMIT = 4
 MLA_MAX_SPLITS = 256
+MLA_NOALLOC_MAX_PAIRS = 256
 
 # Shapes the kernels are written for.
 H, D_C, D_R, D_H, D_V, BLOCK = 128, 512, 64, 128, 128, 64
@@ -31,6 +33,7 @@ EXPORTED = (
     "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
     "mla_cache_append_workspace_bytes", "mla_query_project", "mla_query_project_workspace_bytes",
     "mla_output_project", "mla_output_project_workspace_bytes", "mla_hbm_read_probe",
+    "mla_decode_noalloc",
 )
 
 
@@ -126,7 +129,9 @@ def load():
     lib.mla_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, P]
     lib.mla_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_prefill.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, I, F, P]
-    for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill"):
+    lib.mla_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
+    for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill",
+               "mla_decode_noalloc"):
         getattr(lib, fn).restype = I
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = Z
@@ -277,6 +282,35 @@ def combine(part_o, part_lse, w_uv, out=None, lse_out=None, want_lse=False):
         _ptr(part_o), _ptr(part_lse), _ptr(w_uv), _ptr(out), _ptr(lse_out),
         b, tq, H, D_C, D_V, s, _stream(dev)))
     return (out, lse_out) if lse_out is not None else out
+
+
+def decode_noalloc(q_lat, q_r, kv_cache, block_table, seq_lens, w_uv, softmax_scale, splits,
+                   out, lse_out=None):
+    """mla_decode_paged + mla_combine with the split partials in the library's
+    own device buffer (no allocation by the library; `out` and `lse_out` are
+    the caller's).  Requires splits * B * Tq <= MLA_NOALLOC_MAX_PAIRS."""
+    b, tq = q_lat.shape[0], q_lat.shape[1]
+    _need(q_lat, "q_lat", torch.bfloat16, (b, tq, H, D_C))
+    _need(q_r, "q_r", torch.bfloat16, (b, tq, H, D_R))
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (BLOCK, D_C + D_R):
+        raise ValueError(f"kv_cache must be [num_blocks, {BLOCK}, {D_C + D_R}]")
+    _need(kv_cache, "kv_cache", torch.bfloat16)
+    if block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _need(block_table, "block_table", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32, (b,))
+    _need(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    _need(out, "out", torch.bfloat16, (b, tq, H, D_V))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (b, tq, H))
+    dev = _same_device(q_lat, q_r, kv_cache, block_table, seq_lens, w_uv, out, lse_out)
+    if _debug:
+        check_paged_metadata(block_table, seq_lens, kv_cache.shape[0], tq)
+    _check("mla_decode_noalloc", load().mla_decode_noalloc(
+        _ptr(q_lat), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(w_uv),
+        _ptr(out), _ptr(lse_out), b, tq, H, D_C, D_R, D_V, kv_cache.shape[0], BLOCK,
+        block_table.shape[1], ctypes.c_float(softmax_scale), splits, _stream(dev)))
+    return out
 
 
 def decode_step(q_c, q_r, kv_cache, block_table, seq_lens, w_uk, w_uv, softmax_scale,

@@ -26,6 +26,12 @@ extern "C" hipError_t mla_launch_prefill(const uint16_t* q_c, const uint16_t* q_
                                          int B, int T, int max_blocks, float softmax_scale,
                                          hipStream_t stream);
 
+extern "C" hipError_t mla_launch_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_r,
+                                                const uint16_t* kv, const int32_t* block_table,
+                                                const int32_t* seq_lens, const uint16_t* w_uv,
+                                                uint16_t* out, float* lse_out, int B, int Tq,
+                                                int max_blocks, float softmax_scale,
+                                                int num_splits, hipStream_t stream);
 extern "C" hipError_t mla_launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink,
                                                 hipStream_t stream);
 extern "C" int mla_linear_splits(int M, int N, int K);
@@ -74,6 +80,9 @@ const char* mla_strerror(int status) {
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive size or bad workspace/splits";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape outside H=128, d_c=512, d_r=64, d_h=d_v=128, block 64, Tq<=8";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    case MLA_ERR_NOALLOC_LIMIT:
+      return "MLA_ERR_NOALLOC_LIMIT: num_splits * B * Tq exceeds the library-owned partial buffer "
+             "of mla_decode_noalloc (MLA_NOALLOC_MAX_PAIRS)";
     default: return "unknown mla status";
   }
 }
@@ -124,6 +133,27 @@ int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv
   // merge and the up-projection see the B * Tq query rows alike.
   return status_of(mla_launch_combine(part_o, part_lse, w_uv, out, lse_out, B * Tq, num_splits,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, const uint16_t* w_uv,
+                       uint16_t* out, float* lse_out, int B, int Tq, int H, int d_c, int d_r,
+                       int d_v, int num_blocks, int block_size, int max_blocks_per_seq,
+                       float softmax_scale, int num_splits, void* stream) {
+  if (!q_lat || !q_r || !kv_cache || !block_table || !seq_lens || !w_uv || !out)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || Tq <= 0 || H <= 0 || d_c <= 0 || d_r <= 0 || d_v <= 0 || num_blocks <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || !finite_positive(softmax_scale) ||
+      num_splits < 1 || num_splits > MLA_MAX_SPLITS || (long)B * Tq > kMaxRows)
+    return MLA_ERR_INVALID_ARG;
+  if (H != kH || d_c != kDC || d_r != kDR || d_v != kDV || block_size != kBlock || Tq > kMaxTq)
+    return MLA_ERR_UNSUPPORTED;
+  if ((long)Tq > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
+  if ((long)num_splits * B * Tq > MLA_NOALLOC_MAX_PAIRS) return MLA_ERR_NOALLOC_LIMIT;
+  return status_of(mla_launch_decode_noalloc(q_lat, q_r, kv_cache, block_table, seq_lens, w_uv,
+                                             out, lse_out, B, Tq, max_blocks_per_seq,
+                                             softmax_scale, num_splits,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 size_t mla_decode_workspace_bytes(int B, int Tq, int H, int d_c, int num_splits) {

@@ -37,12 +37,12 @@ def test_every_declared_symbol_is_exported():
     assert names
     for fn in names:
         assert hasattr(lib, fn), f"{fn} declared in mla.h but not exported"
-    assert set(names) <= set(api.EXPORTED) | {"mla_decode_paged_noalloc"}
+    assert set(names) == set(api.EXPORTED)
 
 
 def test_strerror_and_version():
     lib = _lib()
-    for code in range(4):
+    for code in range(5):
         assert lib.mla_strerror(code)
     assert b"unknown" in lib.mla_strerror(99)
     assert lib.mla_version() >= 100
@@ -235,3 +235,19 @@ def test_hbm_read_probe_argument_errors():
     assert lib.mla_hbm_read_probe(4096, 0, 16, None) == E               # empty
     assert lib.mla_hbm_read_probe(4096, 1000, 16, None) == E            # not a multiple of 16
     assert lib.mla_hbm_read_probe(4100, 1024, 16, None) == E            # not 16-byte aligned
+
+
+def test_noalloc_argument_errors():
+    """Host checks of the no-allocation decode, including the size limit of its
+    library-owned buffer (no GPU is touched: every call fails before a launch)."""
+    lib = _lib()
+
+    def call(B=2, Tq=1, splits=2, H=128, kv=FAKE):
+        return lib.mla_decode_noalloc(FAKE, FAKE, kv, FAKE, FAKE, FAKE, FAKE, NULL, B, Tq, H, 512,
+                                      64, 128, 10, 64, 5, ctypes.c_float(0.07), splits, NULL)
+    assert call(kv=NULL) == api.MLA_ERR_INVALID_ARG
+    assert call(splits=0) == api.MLA_ERR_INVALID_ARG
+    assert call(H=64) == api.MLA_ERR_UNSUPPORTED
+    assert call(B=64, splits=5) == api.MLA_ERR_NOALLOC_LIMIT       # 320 pairs
+    assert call(B=65, Tq=2, splits=2) == api.MLA_ERR_NOALLOC_LIMIT
+    assert b"NOALLOC_LIMIT" in lib.mla_strerror(api.MLA_ERR_NOALLOC_LIMIT)
