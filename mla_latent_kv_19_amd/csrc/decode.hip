@@ -254,6 +254,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     lds_u8* stage;       // its LDS destination
   };
   auto top = [&](int n, Next& nx) {
+    // Page of tile n+2: a scalar load issued now, so that the wait of the
+    // barrier below covers it (issued after the barrier, its wait stalled the
+    // start of the score product of every wave).
+    const int pg2 = (n + 2 < ntiles) ? table[(T0 + (n + 2) * kTileTok) >> 6] : 0;
     // This wave's rows of tile n have landed (its own direct-to-LDS loads).
     if (n + 1 < ntiles) wait_vmcnt<kLoadsPerThread>(); else wait_vmcnt<0>();
     const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
@@ -275,7 +279,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     lds_barrier();
     nx.g = nullptr;
     if (n + 2 < ntiles) {
-      nx.g = reinterpret_cast<const char*>(tile_rows(n + 2)) + wave * 8 * kRowBytes;
+      nx.g = reinterpret_cast<const char*>(
+                 kv + ((size_t)pg2 * kTok + ((T0 + (n + 2) * kTileTok) & (kTok - 1))) * kRowVals) +
+             wave * 8 * kRowBytes;
       nx.stage = smem + ((n + 2) % kRing) * kTileBytes + wave * kRowGrpBytes;
     }
   };
@@ -372,7 +378,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   };
 
   // Rare rescale, then O^T += V^T . P^T for tile n (32 MFMAs, value operands
-  // read 3 ahead with transposed LDS reads and rotating through 5 registers).
+  // read 3 ahead with transposed LDS reads and rotating through 5 registers;
+  // the two token halves of one accumulator block are multiplied back to
+  // back, ~2 % fewer cycles than 16 blocks apart).
   // With a next tile (scores sp), its softmax runs in pieces between the value
   // MFMAs and leaves P, alpha and the rescale flag for the next call in
   // pb2 / alpha2 / resc2.
@@ -394,12 +402,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     resc2 = false;
     bf16x8 vb[5];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) vb[j] = ld_v(stage, j);
+    // m -> (cb = m >> 1, token half kt = m & 1): the two k-steps of one
+    // accumulator back to back.
+    for (int j = 0; j < 3; ++j) vb[j] = ld_v(stage, ((j & 1) << 4) | (j >> 1));
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                   : "+a"(acc[m & 15]) : "v"(vb[m % 5]), "v"(pb[m >> 4]));
-      if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, m + 3);
+                   : "+a"(acc[m >> 1]) : "v"(vb[m % 5]), "v"(pb[m & 1]));
+      if (m + 3 < 32) vb[(m + 3) % 5] = ld_v(stage, (((m + 3) & 1) << 4) | ((m + 3) >> 1));
       if (with_sm) sm_step(MASK, m, lim, st, sp, pb2, alpha2, resc2);
     }
   };
