@@ -23,6 +23,8 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import struct
 import sys
 import time
 
@@ -34,6 +36,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode KV-tokens/s and TFLOP/s (+% HBM/MFMA roofline), B=64 ctx 32K, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA peak
+# Dense bf16 matrix work the chip retires per shader clock: 256 CUs x 4 SIMDs,
+# each a v_mfma_f32_32x32x16_bf16 (32768 FLOP) every 32 clocks (2.52 PFLOP/s
+# at 2.4 GHz, the published peak).
+BF16_FLOP_PER_CLOCK = 256 * 4 * 32768 / 32
 ROW_BYTES = 576 * 2            # one cached token: latent 512 + rotary key 64, bf16
 FLOP_PER_TOKEN_QUERY = 128 * 2 * (576 + 512)   # scores + value product, all heads
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_paged_headline_traffic.json")
@@ -78,21 +84,63 @@ def parse():
     return ap.parse_args()
 
 
-def decode_source_hash():
-    h = hashlib.sha256()
-    for name in ("decode.hip", "mla_common.h"):
-        with open(os.path.join(ROOT, "mla_latent_kv_19_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def _elf_sections(d):
+    shoff = struct.unpack_from("<Q", d, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+    secs = []
+    for i in range(shnum):
+        name, typ, _, addr, off, size, link, _, _, _ = struct.unpack_from("<IIQQQQIIQQ", d, shoff + i * shentsize)
+        secs.append({"name": name, "typ": typ, "addr": addr, "off": off, "size": size, "link": link})
+    st = secs[shstrndx]
+    for sec in secs:
+        b = d[st["off"] + sec["name"]:]
+        sec["sname"] = b[:b.index(b"\0")].decode()
+    return secs
 
 
-def measured_traffic(bytes_algorithmic):
-    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+def kernel_code_hash(lib_path, pattern=r"decode_paged_kernel"):
+    """sha256 (16 hex digits) of the gfx950 machine code of the kernel whose
+    symbol matches `pattern`, read from the code object bundled in the library:
+    it changes when the kernel's instructions change and not with comments."""
+    d = open(lib_path, "rb").read()
+    fat = [x for x in _elf_sections(d) if x["sname"] == ".hip_fatbin"][0]
+    blob = d[fat["off"]:fat["off"] + fat["size"]]
+    for m in re.finditer(b"__CLANG_OFFLOAD_BUNDLE__", blob):
+        b0 = m.start()
+        n = struct.unpack_from("<Q", blob, b0 + 24)[0]
+        p = b0 + 32
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", blob, p)
+            triple = blob[p + 24:p + 24 + tl].decode()
+            p += 24 + tl
+            if "gfx950" not in triple:
+                continue
+            co = blob[b0 + off:b0 + off + size]
+            secs = _elf_sections(co)
+            text = [x for x in secs if x["sname"] == ".text"][0]
+            for sec in secs:
+                if sec["typ"] != 2:                          # SHT_SYMTAB
+                    continue
+                strs = secs[sec["link"]]
+                for k in range(sec["size"] // 24):
+                    st_name, st_info, _, _, st_value, st_size = struct.unpack_from(
+                        "<IBBHQQ", co, sec["off"] + k * 24)
+                    nb = co[strs["off"] + st_name:]
+                    name = nb[:nb.index(b"\0")].decode()
+                    if (st_info & 0xF) == 2 and re.search(pattern, name):
+                        o = text["off"] + (st_value - text["addr"])
+                        return hashlib.sha256(co[o:o + st_size]).hexdigest()[:16]
+    return None
+
+
+def measured_traffic(lib_path):
+    """HBM bytes per launch from the committed rocprofv3 counters, reported only
+    while the decode kernel's machine code is the one they were taken on."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != decode_source_hash():
+    if rec.get("kernel_code_sha") != kernel_code_hash(lib_path):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -461,6 +509,14 @@ def main():
     t_decode = time_kernel(lambda: api.decode_paged(q_lat, q_r, kv, table, lens, wl.scale, splits,
                                                     part_o, part_lse), n_k)
     t_combine = time_kernel(lambda: api.combine(part_o, part_lse, w_uv, out=out), n_k)
+    # The shader clock the decode kernel runs at: the same kernel through the
+    # library's clocked entry point (each work-group's clock cycles and 100 MHz
+    # ticks, summed on the device), same flush before each launch.
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    t_clocked = time_kernel(lambda: api.decode_paged_clocked(q_lat, q_r, kv, table, lens, wl.scale,
+                                                            splits, part_o, part_lse, clk), n_k)
+    cyc, ticks = (int(v) for v in clk.cpu())
+    clock_ghz = 0.1 * cyc / ticks if ticks else None
     del kflush
 
     kv_bytes = kv_tokens * ROW_BYTES
@@ -470,8 +526,11 @@ def main():
     step_bytes = kv_bytes + weight_bytes + q_bytes + out_bytes
     flops = kv_tokens * Tq * FLOP_PER_TOKEN_QUERY + 2 * B * Tq * 128 * 2 * 128 * 512
     value = kv_tokens / (ms_step * 1e-3)
+    decode_flops = kv_tokens * Tq * FLOP_PER_TOKEN_QUERY
+    mfma_floor_us = (decode_flops / (BF16_FLOP_PER_CLOCK * clock_ghz * 1e9) * 1e6
+                     if clock_ghz else None)
     achieved = kv_bytes / (t_decode * 1e-3) / 1e9
-    traffic = measured_traffic(kv_bytes)
+    traffic = measured_traffic(api.library_path())
     probe_gbs = read_probe(kv_bytes)
     res = {
         "metric": METRIC,
@@ -507,7 +566,11 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes,
-            "mfma_tflops": kv_tokens * Tq * FLOP_PER_TOKEN_QUERY / (t_decode * 1e-3) / 1e12,
+            "mfma_tflops": decode_flops / (t_decode * 1e-3) / 1e12,
+            "clock_ghz": clock_ghz,
+            "clocked_launch_ms": t_clocked,
+            "mfma_floor_us_at_clock": mfma_floor_us,
+            "mfma_frac_at_clock": (mfma_floor_us / (t_clocked * 1e3)) if mfma_floor_us else None,
             "read_probe_gbs": probe_gbs,
             "frac_of_read_probe": achieved / probe_gbs,
         },

@@ -320,6 +320,25 @@ int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size,
  */
 int mla_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Measurement utility, not part of the attention path: mla_decode_paged
+ * (same kernel, same arguments and results) that also ADDS to clock_sums
+ * (device uint64[2], 8-byte aligned, not cleared by the call) the sum over
+ * its work-groups of shader-clock cycles (clock_sums[0]) and of 100 MHz
+ * real-time ticks (clock_sums[1]) from each work-group's start to its end.
+ * 0.1 GHz * clock_sums[0] / clock_sums[1] is the average shader clock the
+ * kernel ran at; the bench sets its matrix-unit floor against it.  NULL or a
+ * misaligned clock_sums returns MLA_ERR_INVALID_ARG; otherwise as
+ * mla_decode_paged.
+ */
+int mla_decode_paged_clocked(const uint16_t* q_lat, const uint16_t* q_r,
+                             const uint16_t* kv_cache, const int32_t* block_table,
+                             const int32_t* seq_lens,
+                             int B, int Tq, int H, int d_c, int d_r,
+                             int num_blocks, int block_size, int max_blocks_per_seq,
+                             float softmax_scale, int num_splits,
+                             float* part_o, float* part_lse, uint64_t* clock_sums, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ EXPORTED = (
     "mla_prefill_workspace_bytes", "mla_decode_num_splits", "mla_cache_append",
     "mla_cache_append_workspace_bytes", "mla_query_project", "mla_query_project_workspace_bytes",
     "mla_output_project", "mla_output_project_workspace_bytes", "mla_hbm_read_probe",
-    "mla_decode_noalloc",
+    "mla_decode_noalloc", "mla_decode_paged_clocked",
 )
 
 
@@ -129,6 +129,8 @@ def load():
     lib.mla_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, P]
     lib.mla_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_prefill.argtypes = [P, P, P, P, P, P, P, P, P, Z, I, I, I, I, I, I, I, I, I, I, F, P]
+    lib.mla_decode_paged_clocked.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, P, P, P]
+    lib.mla_decode_paged_clocked.restype = I
     lib.mla_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
     for fn in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_prefill",
                "mla_decode_noalloc"):
@@ -262,6 +264,23 @@ def decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, softmax_scale, spl
         b, tq, H, D_C, D_R, kv_cache.shape[0], BLOCK, block_table.shape[1],
         ctypes.c_float(softmax_scale), splits, _ptr(part_o), _ptr(part_lse), _stream(dev)))
     return part_o, part_lse
+
+
+def decode_paged_clocked(q_lat, q_r, kv_cache, block_table, seq_lens, softmax_scale, splits,
+                         part_o, part_lse, clock_sums):
+    """decode_paged (same kernel) that also adds its work-groups' shader-clock
+    cycles and 100 MHz ticks to clock_sums (int64 [2] on the device)."""
+    b, tq = q_lat.shape[0], q_lat.shape[1]
+    _need(clock_sums, "clock_sums", torch.int64, (2,))
+    _need(part_o, "part_o", torch.float32, (splits, b, tq, H, D_C))
+    _need(part_lse, "part_lse", torch.float32, (splits, b, tq, H))
+    dev = _same_device(q_lat, q_r, kv_cache, block_table, seq_lens, part_o, part_lse, clock_sums)
+    _check("mla_decode_paged_clocked", load().mla_decode_paged_clocked(
+        _ptr(q_lat), _ptr(q_r), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+        b, tq, H, D_C, D_R, kv_cache.shape[0], BLOCK, block_table.shape[1],
+        ctypes.c_float(softmax_scale), splits, _ptr(part_o), _ptr(part_lse), _ptr(clock_sums),
+        _stream(dev)))
+    return clock_sums
 
 
 def combine(part_o, part_lse, w_uv, out=None, lse_out=None, want_lse=False):

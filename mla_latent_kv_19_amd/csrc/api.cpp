@@ -15,7 +15,8 @@ extern "C" hipError_t mla_launch_decode_paged(const uint16_t* q_lat, const uint1
                                               const uint16_t* kv, const int32_t* block_table,
                                               const int32_t* seq_lens, int B, int Tq, int max_blocks,
                                               float softmax_scale, int num_splits, float* part_o,
-                                              float* part_lse, hipStream_t stream);
+                                              float* part_lse, unsigned long long* clk,
+                                              hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_lse,
                                          const uint16_t* w_uv, uint16_t* out, float* lse_out, int M,
                                          int S, hipStream_t stream);
@@ -103,11 +104,12 @@ int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat, int
   return status_of(mla_launch_absorb_q(q_c, w_uk, q_lat, M, static_cast<hipStream_t>(stream)));
 }
 
-int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
-                     const int32_t* block_table, const int32_t* seq_lens, int B, int Tq, int H,
-                     int d_c, int d_r, int num_blocks, int block_size, int max_blocks_per_seq,
-                     float softmax_scale, int num_splits, float* part_o, float* part_lse,
-                     void* stream) {
+namespace {
+int decode_paged_checked(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
+                         const int32_t* block_table, const int32_t* seq_lens, int B, int Tq, int H,
+                         int d_c, int d_r, int num_blocks, int block_size, int max_blocks_per_seq,
+                         float softmax_scale, int num_splits, float* part_o, float* part_lse,
+                         unsigned long long* clk, void* stream) {
   if (!q_lat || !q_r || !kv_cache || !block_table || !seq_lens || !part_o || !part_lse)
     return MLA_ERR_INVALID_ARG;
   if (B <= 0 || Tq <= 0 || H <= 0 || d_c <= 0 || d_r <= 0 || num_blocks <= 0 || block_size <= 0 ||
@@ -119,7 +121,30 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t*
   if ((long)Tq > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
   return status_of(mla_launch_decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq,
                                            max_blocks_per_seq, softmax_scale, num_splits, part_o,
-                                           part_lse, static_cast<hipStream_t>(stream)));
+                                           part_lse, clk, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, int B, int Tq, int H,
+                     int d_c, int d_r, int num_blocks, int block_size, int max_blocks_per_seq,
+                     float softmax_scale, int num_splits, float* part_o, float* part_lse,
+                     void* stream) {
+  return decode_paged_checked(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq, H, d_c, d_r,
+                              num_blocks, block_size, max_blocks_per_seq, softmax_scale,
+                              num_splits, part_o, part_lse, nullptr, stream);
+}
+
+int mla_decode_paged_clocked(const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int B, int Tq,
+                             int H, int d_c, int d_r, int num_blocks, int block_size,
+                             int max_blocks_per_seq, float softmax_scale, int num_splits,
+                             float* part_o, float* part_lse, uint64_t* clock_sums, void* stream) {
+  if (!clock_sums || (reinterpret_cast<uintptr_t>(clock_sums) & 7) != 0) return MLA_ERR_INVALID_ARG;
+  return decode_paged_checked(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq, H, d_c, d_r,
+                              num_blocks, block_size, max_blocks_per_seq, softmax_scale,
+                              num_splits, part_o, part_lse,
+                              reinterpret_cast<unsigned long long*>(clock_sums), stream);
 }
 
 int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv, uint16_t* out,

@@ -121,8 +121,16 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ q_r,
     const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int B, int Tq, int max_blocks, float scale_log2,
-    int num_splits, int num_units, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int num_splits, int num_units, float* __restrict__ part_o, float* __restrict__ part_lse,
+    unsigned long long* __restrict__ clk) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dec_smem[];
+  // Measurement only (clk is null in normal use): shader-clock cycles and
+  // 100 MHz real-time ticks of this work-group, summed into clk[0] / clk[1].
+  unsigned long long c0 = 0, r0 = 0;
+  if (clk != nullptr) {
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   lds_u8* smem = to_lds(dec_smem);
   lds_u8* qr_lds = smem + kRing * kTileBytes;
 
@@ -480,6 +488,12 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
           make_float4(acc[cb][4 * a] * inv, acc[cb][4 * a + 1] * inv, acc[cb][4 * a + 2] * inv,
                       acc[cb][4 * a + 3] * inv);
   if (half == 0) *lse_dst = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+  if (clk != nullptr && tid == 0) {
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    atomicAdd(clk, c1 - c0);
+    atomicAdd(clk + 1, r1 - r0);
+  }
 }
 
 }  // namespace mla
@@ -487,7 +501,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
 extern "C" hipError_t mla_launch_decode_paged(
     const uint16_t* q_lat, const uint16_t* q_r, const uint16_t* kv, const int32_t* block_table,
     const int32_t* seq_lens, int B, int Tq, int max_blocks, float softmax_scale, int num_splits,
-    float* part_o, float* part_lse, hipStream_t stream) {
+    float* part_o, float* part_lse, unsigned long long* clk, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&mla::decode_paged_kernel),
       hipFuncAttributeMaxDynamicSharedMemorySize, mla::kDecLdsBytes);
@@ -496,7 +510,7 @@ extern "C" hipError_t mla_launch_decode_paged(
   const int grid = ((num_units + 7) / 8) * 8 * Tq;
   float scale_log2 = softmax_scale * mla::kLog2e;
   void* args[] = {&q_lat, &q_r, &kv, &block_table, &seq_lens, &B, &Tq, &max_blocks,
-                  &scale_log2, &num_splits, const_cast<int*>(&num_units), &part_o, &part_lse};
+                  &scale_log2, &num_splits, const_cast<int*>(&num_units), &part_o, &part_lse, &clk};
   return hipLaunchKernel(reinterpret_cast<const void*>(&mla::decode_paged_kernel), dim3(grid),
                          dim3(mla::kDecThreads), args, mla::kDecLdsBytes, stream);
 }

@@ -27,7 +27,8 @@ extern "C" hipError_t mla_launch_decode_paged(const uint16_t* q_lat, const uint1
                                               const uint16_t* kv, const int32_t* block_table,
                                               const int32_t* seq_lens, int B, int Tq, int max_blocks,
                                               float softmax_scale, int num_splits, float* part_o,
-                                              float* part_lse, hipStream_t stream);
+                                              float* part_lse, unsigned long long* clk,
+                                              hipStream_t stream);
 extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_lse,
                                          const uint16_t* w_uv, uint16_t* out, float* lse_out, int M,
                                          int S, hipStream_t stream);
@@ -88,7 +89,7 @@ extern "C" hipError_t mla_launch_decode_noalloc(const uint16_t* q_lat, const uin
   float* part_o = base;
   float* part_lse = base + kPartOFloats;
   err = mla_launch_decode_paged(q_lat, q_r, kv, block_table, seq_lens, B, Tq, max_blocks,
-                                softmax_scale, num_splits, part_o, part_lse, stream);
+                                softmax_scale, num_splits, part_o, part_lse, nullptr, stream);
   if (err != hipSuccess) return err;
   return mla_launch_combine(part_o, part_lse, w_uv, out, lse_out, B * Tq, num_splits, stream);
 }

@@ -251,3 +251,15 @@ def test_noalloc_argument_errors():
     assert call(B=64, splits=5) == api.MLA_ERR_NOALLOC_LIMIT       # 320 pairs
     assert call(B=65, Tq=2, splits=2) == api.MLA_ERR_NOALLOC_LIMIT
     assert b"NOALLOC_LIMIT" in lib.mla_strerror(api.MLA_ERR_NOALLOC_LIMIT)
+
+
+def test_clocked_decode_argument_errors():
+    lib = _lib()
+    base = dict(B=2, Tq=1, H=128)
+
+    def call(clock, H=128):
+        return lib.mla_decode_paged_clocked(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 1, H, 512, 64, 10, 64,
+                                            5, ctypes.c_float(0.07), 2, FAKE, FAKE, clock, NULL)
+    assert call(NULL) == api.MLA_ERR_INVALID_ARG
+    assert call(ctypes.c_void_p(0x1004)) == api.MLA_ERR_INVALID_ARG      # not 8-byte aligned
+    assert call(FAKE, H=64) == api.MLA_ERR_UNSUPPORTED

@@ -373,3 +373,23 @@ def test_debug_mode_rejects_bad_metadata():
                             wl.scale, splits=2)
     finally:
         api.set_debug(prev)
+
+
+def test_clocked_decode_matches_and_reports_a_clock():
+    """The clocked measurement entry point runs the same kernel: bit-identical
+    partials, and the summed cycles / 100 MHz ticks give a clock between 0.1
+    and 3 GHz."""
+    print("[case] clocked decode", flush=True)
+    wl = synth.small_workload(batch=4, tq=2, len_lo=2, len_hi=900, seed=161)
+    inp = make(wl)
+    dev = DevInputs(inp)
+    q_lat = api.absorb_q(dev.q_c, dev.w_uk)
+    po, pl = api.decode_paged(q_lat, dev.q_r, dev.kv, dev.table, dev.lens, wl.scale, 3)
+    po2, pl2 = torch.empty_like(po), torch.empty_like(pl)
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    api.decode_paged_clocked(q_lat, dev.q_r, dev.kv, dev.table, dev.lens, wl.scale, 3, po2, pl2, clk)
+    torch.cuda.synchronize()
+    assert torch.equal(po, po2) and torch.equal(pl, pl2)
+    cyc, ticks = (int(v) for v in clk.cpu())
+    assert cyc > 0 and ticks > 0
+    assert 0.1 < 0.1 * cyc / ticks < 3.0
