@@ -49,6 +49,7 @@ constexpr int kDecLdsBytes = kRing * kTileBytes + kQrBytes;      // 163840
 
 static_assert(kLoadsPerThread * 16 * kDecThreads == kTileBytes, "tile must split evenly");
 static_assert(kDecLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(4 * 32 * (256 + 4) * 4 <= kRing * kTileBytes, "epilogue transpose area inside the ring");
 
 // Lazy renormalisation threshold (log2 units): unnormalised weights stay <= 2^8.
 constexpr float kLazy = 8.f;
@@ -173,16 +174,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
 
   const size_t qrow = (size_t)(b * Tq + qi) * 128;          // first row of this query's heads
   const size_t row = qrow + head;
-  float* o_dst = part_o + ((size_t)split * B * Tq * 128 + row) * 512;
   float* lse_dst = part_lse + (size_t)split * B * Tq * 128 + row;
 
   if (ntiles == 0) {
-    // Nothing visible in this split: o = 0, lse = -inf.
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(o_dst + cb * 32 + 8 * a + 4 * half) = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Nothing visible in this split: o = 0, lse = -inf (wave w: the rows of
+    // its 32 heads, contiguous 1 KB stores).
+    float* o_rows = part_o + ((size_t)split * B * Tq * 128 + qrow + wave * 32) * 512;
+    for (int i = lane; i < 32 * 128; i += 64)
+      *reinterpret_cast<float4*>(o_rows + (size_t)(i >> 7) * 512 + (i & 127) * 4) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
     if (half == 0) *lse_dst = -INFINITY;
     return;
   }
@@ -480,13 +480,34 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   agpr_settle16(acc);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  // Partial o_s out through LDS: lane = head holds 4-column pieces of its
+  // head's row, so stored directly every instruction would touch 32 rows; the
+  // wave writes its O^T into a [32 heads][256 + 4] fp32 area of the (now idle)
+  // ring and reads it back a head row at a time, so every global store is one
+  // contiguous 1 KB.  Two rounds of 256 columns; each wave uses its own area.
+  constexpr int kOPitchF = 256 + 4;                  // floats per row: conflict-free writes
+  lds_barrier();                                     // every wave is done with the ring
+  lds_u8* o_lds = smem + wave * 32 * kOPitchF * 4;
+  float* o_row0 = part_o + ((size_t)split * B * Tq * 128 + qrow + wave * 32) * 512;
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
+  for (int rnd = 0; rnd < 2; ++rnd) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      *reinterpret_cast<float4*>(o_dst + cb * 32 + 8 * a + 4 * half) =
-          make_float4(acc[cb][4 * a] * inv, acc[cb][4 * a + 1] * inv, acc[cb][4 * a + 2] * inv,
-                      acc[cb][4 * a + 3] * inv);
+    for (int c8 = 0; c8 < 8; ++c8)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int cb = 8 * rnd + c8;
+        const f32x4 v = {acc[cb][4 * a] * inv, acc[cb][4 * a + 1] * inv, acc[cb][4 * a + 2] * inv,
+                         acc[cb][4 * a + 3] * inv};
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
+            o_lds + (l32 * kOPitchF + c8 * 32 + 8 * a + 4 * half) * 4) = v;
+      }
+#pragma unroll 4
+    for (int h = 0; h < 32; ++h) {
+      const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          o_lds + (h * kOPitchF + 4 * lane) * 4);
+      *reinterpret_cast<f32x4*>(o_row0 + (size_t)h * 512 + 256 * rnd + 4 * lane) = v;
+    }
+  }
   if (half == 0) *lse_dst = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   if (clk != nullptr && tid == 0) {
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
