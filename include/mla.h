@@ -115,15 +115,30 @@ int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat,
  * q_r    bf16 [B, Tq, H, d_r]   rotary part of the query, already rotated
  * kv_cache, block_table, seq_lens as described above (read only)
  * softmax_scale: score scale (1/sqrt(192) for DeepSeek-V3's dims), finite > 0
- * num_splits S in [1, MLA_MAX_SPLITS]: each sequence's ceil(L_b / block_size)
- *   blocks are cut into S contiguous ranges of ceil(blocks / S) blocks
- *   (trailing ranges may be empty)
- * part_o   fp32 [S, B, Tq, H, d_c]  written: o_s, normalised within its split
- * part_lse fp32 [S, B, Tq, H]       written: ln sum_{t in split} e^{s_t}
+ * num_splits S in [1, MLA_MAX_SPLITS]: partial slots per (sequence, query).
+ *   S = 1: each sequence is attended whole, slot 0.
+ *   S > 1 and B * Tq < 64: each sequence's ceil(L_b / block_size) blocks are
+ *   cut into S contiguous ranges of ceil(blocks / S) blocks, range j in slot
+ *   j (trailing ranges may be empty).
+ *   S > 1 and B * Tq >= 64: the split is token-balanced over the batch,
+ *   planned on the device from seq_lens: the sequences' blocks are laid end
+ *   to end (each sequence charged 6 blocks more for its fixed per-split cost,
+ *   unless all sequences have the same block count) and cut into equal
+ *   chunks, as many as the device holds work-groups at once (its compute
+ *   units / Tq, at most B * S), but no shorter than ceil(longest / (S - 1))
+ *   blocks, so that each sequence meets at most S chunks.  Sequence b's part
+ *   of chunk u goes to slot u - (chunk of its first block); its slots past
+ *   the last are empty.
+ * part_o   fp32 [S, B, Tq, H, d_c]  written for non-empty slots: o_s,
+ *          normalised within its slot; rows of empty slots are not written
+ * part_lse fp32 [S, B, Tq, H]       written for every slot:
+ *          ln sum_{t in slot} e^{s_t}, -inf for an empty slot
  * (both may be carved from one buffer of mla_decode_workspace_bytes bytes).
  * Errors: MLA_ERR_INVALID_ARG for NULL pointers, non-positive sizes, a
- * non-finite or non-positive scale, S out of range, B * Tq > 65536 or
- * Tq > max_blocks_per_seq * block_size; MLA_ERR_UNSUPPORTED for other dims.
+ * non-finite or non-positive scale, S out of range, B * Tq > 65536,
+ * Tq > max_blocks_per_seq * block_size, a row of more than 2^31 - 1 tokens
+ * or B * (max_blocks_per_seq + 6) > 2^31 - 1; MLA_ERR_UNSUPPORTED for other
+ * dims.
  */
 int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
                      const uint16_t* kv_cache, const int32_t* block_table,
@@ -140,7 +155,8 @@ int mla_decode_paged(const uint16_t* q_lat, const uint16_t* q_r,
  * box "Output projection" (the value up-projection folds into the output
  * side); "Teardown: DeepSeek-V3", section 4 (v_C = W_UV c).
  * part_o, part_lse as written by mla_decode_paged for the same B, Tq and
- *         num_splits (read only; rows of empty splits may hold anything)
+ *         num_splits (read only; the part_o row of a slot whose lse is -inf
+ *         is not read and may hold anything)
  * w_uv    bf16 [H, d_c, d_v], read only
  * out     bf16 [B, Tq, H, d_v]   written
  * lse_out fp32 [B, Tq, H] or NULL: ln sum over all splits (natural log)
@@ -294,15 +310,16 @@ size_t mla_decode_part_lse_bytes(int B, int Tq, int H, int num_splits);
 size_t mla_prefill_workspace_bytes(long total_kv_tokens, int H, int d_h, int d_v);
 
 /*
- * Suggested num_splits for a decode step: enough work-groups (one per
- * sequence, split and group of 128 query rows) to cover `num_cus` compute
- * units about once, never more splits than the longest sequence has blocks,
- * and at most MLA_MAX_SPLITS.  Host-only arithmetic; returns 0 on invalid
- * arguments.  It sees only the longest length: with strongly ragged lengths,
- * about twice that many work-groups can balance better (two rounds, which the
- * hardware schedules as compute units free up), at the cost of twice the
- * partial-result traffic; e.g. B = 64, Tq = 2, L ~ U[4096, 8192] on MI355X:
- * 4 splits 277 us per step against 296 us for the suggested 2.
+ * Suggested num_splits (partial slots) for a decode step.  With at least
+ * two rounds of work-groups in whole sequences (B * Tq >= 2 num_cus), or
+ * sequences of one block, it is 1.
+ * Otherwise, with c = ceil(num_cus / (B * Tq)) splits per sequence (capped
+ * at the longest sequence's block count) filling the compute units about
+ * once: c for B * Tq < 64 (equal ranges per sequence); from B * Tq = 64 on
+ * (token-balanced chunks), 2c + 1 (room for sequences up to twice the mean
+ * length, plus a chunk that straddles two sequences) where that is at most
+ * 40, the slots the combine reads in one round trip, else c + 1; at most
+ * MLA_MAX_SPLITS.  Host-only arithmetic; returns 0 on invalid arguments.
  */
 int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size,
                           int num_cus);

@@ -3,6 +3,7 @@
 // only validates and dispatches.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -71,6 +72,17 @@ int status_of(hipError_t e) {
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
 
+// Decode metadata sizes the kernels' int arithmetic holds: Tq keys fit the
+// table row, a row's token count max_blocks * block_size fits an int, and so
+// does the split plan's total cost, B * (max_blocks + 6) pages (6: the
+// plan's per-sequence cost; the block table then has fewer than 2^31
+// entries).
+bool plan_fits(int B, int Tq, int max_blocks_per_seq, int block_size) {
+  const long row_tokens = (long)max_blocks_per_seq * block_size;
+  return (long)Tq <= row_tokens && row_tokens <= INT_MAX &&
+         (long)B * ((long)max_blocks_per_seq + 6) <= INT_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,7 +130,7 @@ int decode_paged_checked(const uint16_t* q_lat, const uint16_t* q_r, const uint1
     return MLA_ERR_INVALID_ARG;
   if (H != kH || d_c != kDC || d_r != kDR || block_size != kBlock || Tq > kMaxTq)
     return MLA_ERR_UNSUPPORTED;
-  if ((long)Tq > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
+  if (!plan_fits(B, Tq, max_blocks_per_seq, block_size)) return MLA_ERR_INVALID_ARG;
   return status_of(mla_launch_decode_paged(q_lat, q_r, kv_cache, block_table, seq_lens, B, Tq,
                                            max_blocks_per_seq, softmax_scale, num_splits, part_o,
                                            part_lse, clk, static_cast<hipStream_t>(stream)));
@@ -173,7 +185,7 @@ int mla_decode_noalloc(const uint16_t* q_lat, const uint16_t* q_r, const uint16_
     return MLA_ERR_INVALID_ARG;
   if (H != kH || d_c != kDC || d_r != kDR || d_v != kDV || block_size != kBlock || Tq > kMaxTq)
     return MLA_ERR_UNSUPPORTED;
-  if ((long)Tq > (long)max_blocks_per_seq * block_size) return MLA_ERR_INVALID_ARG;
+  if (!plan_fits(B, Tq, max_blocks_per_seq, block_size)) return MLA_ERR_INVALID_ARG;
   if ((long)num_splits * B * Tq > MLA_NOALLOC_MAX_PAIRS) return MLA_ERR_NOALLOC_LIMIT;
   return status_of(mla_launch_decode_noalloc(q_lat, q_r, kv_cache, block_table, seq_lens, w_uv,
                                              out, lse_out, B, Tq, max_blocks_per_seq,
@@ -301,12 +313,24 @@ int mla_output_project(const uint16_t* o, const uint16_t* w_o, uint16_t* y, void
 
 int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size, int num_cus) {
   if (B <= 0 || Tq <= 0 || H <= 0 || max_seq_len <= 0 || block_size <= 0 || num_cus <= 0) return 0;
-  const long groups = (long)B * (((long)Tq * H + 127) / 128);    // work-groups per split
+  const long groups = (long)B * (((long)Tq * H + 127) / 128);    // work-groups per unit of work
   const long pages = (max_seq_len + block_size - 1) / block_size;
-  long s = (num_cus + groups - 1) / groups;
-  if (s > pages) s = pages;
+  // Two or more rounds of whole sequences fill the chip by themselves, and a
+  // single block cannot be cut.
+  if (groups >= 2L * num_cus || pages == 1) return 1;
+  // c splits per sequence fill the chip about once.  Below 64 query rows the
+  // decode cuts each sequence into num_splits equal ranges: c.  From 64 rows
+  // on it balances the batch's tokens: 2c (room for sequences up to twice the
+  // mean length), plus one for a chunk that straddles two sequences, where
+  // that is at most 40 (the slots the combine reads in one round trip), else
+  // c + 1.
+  const long c = (num_cus + groups - 1) / groups;
+  long s = (c < pages ? c : pages);
+  if (B * (long)Tq >= 64) {
+    const long s2 = (2 * c < pages ? 2 * c : pages) + 1;
+    s = (s2 <= 40) ? s2 : s + 1;
+  }
   if (s > MLA_MAX_SPLITS) s = MLA_MAX_SPLITS;
-  if (s < 1) s = 1;
   return (int)s;
 }
 

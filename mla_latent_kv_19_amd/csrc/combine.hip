@@ -24,6 +24,8 @@ constexpr int kCmbThreads = 256;
 constexpr int kOPitch = 512 + 8;     // bf16 per o_lat LDS row (1040 B)
 constexpr int kWPitch = 128 + 32;    // bf16 per W_UV LDS row (320 B: rows 16 banks apart,
                                      // so the 4 rows of a transposed read hit disjoint banks)
+constexpr int kLseLoads = 5;         // split log-sum-exps per thread in the first round trip
+constexpr int kWtsMin = kLseLoads * kCmbThreads;   // weight slots always present (40 splits)
 
 __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -34,6 +36,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   uint16_t* o_lo = o_hi + 32 * kOPitch;                               // [32][kOPitch]
   uint16_t* wt = o_lo + 32 * kOPitch;                                 // [128][kWPitch]
   float* wts = reinterpret_cast<float*>(wt + 128 * kWPitch);          // [S][32]
+  int* s_end_lds = reinterpret_cast<int*>(wts + (S * 32 > kWtsMin ? S * 32 : kWtsMin));  // 1 + last split of weight > 0
 
   const int h = blockIdx.x % 128;
   const int m0 = (blockIdx.x / 128) * 32;
@@ -72,27 +75,28 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   };
   WSlice w0, w1, w2;
 
-  // 1. Split weights per row.  All threads load the split log-sum-exps (four
+  // 1. Split weights per row.  All threads load the split log-sum-exps (five
   // each, unconditionally from clamped addresses), then the first W_UV slice is
-  // put in flight, then the log-sum-exps go to LDS (wts has at least 1024
-  // slots, so the stores need no test and the loads cannot be moved into one)
-  // and one thread per row normalises them: one memory round trip for up to
-  // 32 splits.
+  // put in flight, then the log-sum-exps go to LDS (wts has at least
+  // kWtsMin slots, so the stores need no test and the loads cannot be moved
+  // into one) and one thread per row normalises them: one memory round trip
+  // for up to 40 splits.  The same threads find the last split of non-zero
+  // weight over the block's rows; step 2 stops there.
   const int n_l = S * 32;
-  float lv[4];
+  float lv[kLseLoads];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
     const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), M - 1);
     lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
   }
   load_w(0, w0);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
     wts[i] = (i < n_l && m0 + (i & 31) < M) ? lv[k] : -INFINITY;
   }
-  for (int i = tid + 4 * kCmbThreads; i < n_l; i += kCmbThreads) {
+  for (int i = tid + kLseLoads * kCmbThreads; i < n_l; i += kCmbThreads) {
     const int sp = i >> 5, r = i & 31;
     wts[i] = (m0 + r < M) ? part_lse[sp * split_stride + (size_t)(m0 + r) * 128 + h] : -INFINITY;
   }
@@ -109,7 +113,15 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
         z += w;
       }
     const float inv = (z > 0.f) ? 1.f / z : 0.f;
-    for (int sp = 0; sp < S; ++sp) wts[sp * 32 + tid] = (mx != -INFINITY) ? wts[sp * 32 + tid] * inv : 0.f;
+    int last = -1;
+    for (int sp = 0; sp < S; ++sp) {
+      const float w = (mx != -INFINITY) ? wts[sp * 32 + tid] * inv : 0.f;
+      wts[sp * 32 + tid] = w;
+      if (w != 0.f) last = sp;
+    }
+#pragma unroll
+    for (int d = 16; d > 0; d >>= 1) last = max(last, __shfl_xor(last, d, 32));
+    if (tid == 0) *s_end_lds = last + 1;
     if (lse_out != nullptr && m < M)
       lse_out[(size_t)m * 128 + h] = (mx != -INFINITY) ? mx + __logf(z) : -INFINITY;
   }
@@ -122,8 +134,12 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   // pair of waves): its LDS rows only feed output rows >= M, which are never
   // written.  When the block has at most eight rows below M, both pairs of
   // waves work on them, each on every second split, and their fp32 sums meet
-  // in the (not yet used) W_UV staging area.  A split of weight 0 (empty,
-  // whose partial may hold anything) is dropped by a select, not a branch.
+  // in the (not yet used) W_UV staging area.  Splits past the block's last
+  // one of non-zero weight are not visited; a split of weight 0 before it
+  // (empty: lse = -inf, its partial never written) is read and dropped by a
+  // select, not a branch, which keeps the loads of eight rows and two splits
+  // in flight together (reading split 0's row in its place, or testing the
+  // weight first, measured slower).
   {
     const int cq = tid & 127, hh = tid >> 7;
     const bool pair = M - m0 <= 8;                      // uniform over the work-group
@@ -144,11 +160,12 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
       const int r0 = pair ? 0 : hh * 8 + 16 * it;
       if (pair ? it > 0 : m0 + r0 >= M) continue;
       const int s_first = pair ? hh : 0, s_step = pair ? 2 : 1;
+      const int s_stop = *s_end_lds;
       float4 o[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 2
-      for (int s = s_first; s < S; s += s_step) {
+      for (int s = s_first; s < s_stop; s += s_step) {
         float4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -239,7 +256,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 }
 
 size_t combine_lds_bytes(int S) {
-  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)(S > 32 ? S : 32) * 32 * 4;
+  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)(S * 32 > kWtsMin ? S * 32 : kWtsMin) * 4 + 16;
 }
 
 }  // namespace mla

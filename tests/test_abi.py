@@ -86,6 +86,10 @@ def test_decode_argument_errors():
     assert _decode(lib, Tq=9) == U
     assert _decode(lib, d_r=32) == U
     assert _decode(lib, B=40000, Tq=2) == E                   # more than 65,536 query rows
+    # Sizes past the split plan's int arithmetic: a row of 2^31 tokens, or
+    # B * (max_blocks + 6) above 2^31 - 1 (1024 * (2^21 + 5) = 2^31 + 5120).
+    assert _decode(lib, max_blocks=1 << 25) == E
+    assert _decode(lib, B=1024, max_blocks=(1 << 21) - 1) == E
 
 
 def test_combine_argument_errors():
@@ -126,14 +130,27 @@ def test_workspace_sizes_and_split_heuristic():
     assert lib.mla_decode_workspace_bytes(64, 1, 128, 512, 4) == 4 * 64 * 128 * 513 * 4
     assert lib.mla_decode_workspace_bytes(1, 1, 128, 512, 1) == 128 * 512 * 4 + 128 * 4
     assert lib.mla_decode_workspace_bytes(0, 1, 128, 512, 1) == 0
-    # 64 sequences on 256 compute units: 4 splits; 8 long sequences: 32 splits.
-    assert lib.mla_decode_num_splits(64, 1, 128, 32768, 64, 256) == 4
+    # Below 64 query rows, the splits per sequence that fill 256 compute
+    # units once (equal ranges): 32 sequences 8, 8 long sequences 32.  From 64
+    # rows on (token-balanced), twice that plus one for a straddling chunk:
+    # 64 sequences 2 * 4 + 1, 64 two-query sequences 2 * 2 + 1.
+    assert lib.mla_decode_num_splits(32, 1, 128, 4096, 64, 256) == 8
     assert lib.mla_decode_num_splits(8, 1, 128, 163840, 64, 256) == 32
-    assert lib.mla_decode_num_splits(64, 2, 128, 8192, 64, 256) == 2
+    assert lib.mla_decode_num_splits(64, 1, 128, 32768, 64, 256) == 9
+    assert lib.mla_decode_num_splits(64, 2, 128, 8192, 64, 256) == 5
+    # Past 40 slots the balanced form keeps one chunk of slack: 80 rows on 4096 units.
+    assert lib.mla_decode_num_splits(80, 1, 128, 163840, 64, 4096) == 53
     # Never more splits than blocks of the longest sequence.
     assert lib.mla_decode_num_splits(1, 1, 128, 1024, 64, 256) == 16
+    assert lib.mla_decode_num_splits(4, 1, 128, 128, 64, 256) == 2
+    assert lib.mla_decode_num_splits(64, 1, 128, 128, 64, 256) == 3
+    # One block, or two rounds of whole sequences: one slot.
     assert lib.mla_decode_num_splits(1, 1, 128, 1, 64, 256) == 1
+    assert lib.mla_decode_num_splits(512, 1, 128, 32768, 64, 256) == 1
+    assert lib.mla_decode_num_splits(256, 2, 128, 32768, 64, 256) == 1
     assert lib.mla_decode_num_splits(0, 1, 128, 1, 64, 256) == 0
+    # The cap.
+    assert lib.mla_decode_num_splits(1, 1, 128, 1 << 24, 64, 8192) == 256
 
 
 def _append(lib, **kw):

@@ -144,11 +144,12 @@ def test_combine_row_blocks(batch, tq, splits):
 
 
 def test_max_split_count():
-    """num_splits = 256 (the maximum): a 16,384-token sequence in 256 splits of
-    one page each beside a 300-token one whose splits are mostly empty, Tq = 2
-    (the combine reads 256 log-sum-exps per row and merges the non-empty
-    splits).  Against the absorbed fp64 form, which is pinned to the
-    un-absorbed oracle to 1e-12."""
+    """num_splits = 256 (the maximum): a 16,384-token sequence beside a
+    300-token one, Tq = 2.  The balanced plan cuts the 265 cost pages into
+    chunks of 3 over about 90 units, so the long sequence fills about 86 slots
+    and both leave the rest empty (the combine reads 256 log-sum-exps per row
+    and merges the non-empty slots).  Against the absorbed fp64 form, which is
+    pinned to the un-absorbed oracle to 1e-12."""
     print("[case] splits=256", flush=True)
     wl = synth.small_workload(batch=2, tq=2, len_lo=2, len_hi=2, seed=57)
     inp = make(wl, seq_lens=[16384, 300])
@@ -156,6 +157,42 @@ def test_max_split_count():
     out, lse = run_decode(dev, splits=256)
     ref, ref_lse = oracle_decode(inp, form="absorbed")
     assert_parity(bf16_to_f64(out), ref, "splits=256")
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_lse))
+    assert np.max(np.abs(got_lse - ref_lse)) <= 2e-2
+
+
+def _balanced_lens(kind, tq, rng):
+    if kind == "one_long":        # one sequence far above the mean: its chunks set the length
+        return [3000] + list(rng.integers(tq, 131, size=32))
+    if kind == "two_steps":       # 70 sequences: the plan's scan takes two 64-lane steps
+        return list(rng.integers(tq, 501, size=70))
+    if kind == "short":           # 140 one- and two-block sequences: several pieces per unit
+        return list(rng.integers(tq, 129, size=140))
+    if kind == "equal_odd":       # equal lengths whose chunks straddle sequences
+        return [65 * 64 - 3] * 7      # 65 blocks: odd, so chunks of 2 or 33 straddle
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind,tq,splits", [
+    ("one_long", 1, None), ("one_long", 1, 2), ("one_long", 2, 3), ("two_steps", 2, None),
+    ("two_steps", 3, 4), ("short", 1, None), ("short", 2, 2), ("equal_odd", 1, None),
+    ("equal_odd", 5, 3)])
+def test_token_balanced_plan(kind, tq, splits):
+    """The device-side token-balanced split: chunks that straddle sequences,
+    units with several pieces, slot counts bound by num_splits (2 and 3 force
+    chunks of ceil(longest / (S - 1)) blocks), a scan over more than 64
+    sequences, and equal lengths (planned without the per-sequence cost).
+    Every query row against the absorbed fp64 form, which is pinned to the
+    un-absorbed oracle to 1e-12."""
+    print(f"[case] balanced plan {kind} tq={tq} splits={splits}", flush=True)
+    rng = np.random.default_rng(900 + tq)
+    lens = _balanced_lens(kind, tq, rng)
+    wl = synth.small_workload(batch=len(lens), tq=tq, len_lo=tq, len_hi=tq, seed=97 + tq)
+    inp = make(wl, seq_lens=lens)
+    out, lse = run_decode(DevInputs(inp), splits=splits)
+    ref, ref_lse = oracle_decode(inp, form="absorbed")
+    assert_parity(bf16_to_f64(out), ref, f"balanced {kind} tq={tq} splits={splits}")
     got_lse = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got_lse))
     assert np.max(np.abs(got_lse - ref_lse)) <= 2e-2
@@ -377,8 +414,9 @@ def test_debug_mode_rejects_bad_metadata():
 
 def test_clocked_decode_matches_and_reports_a_clock():
     """The clocked measurement entry point runs the same kernel: bit-identical
-    partials, and the summed cycles / 100 MHz ticks give a clock between 0.1
-    and 3 GHz."""
+    log-sum-exps and partial outputs of every non-empty slot (an empty slot's
+    output rows are not written), and the summed cycles / 100 MHz ticks give a
+    clock between 0.1 and 3 GHz."""
     print("[case] clocked decode", flush=True)
     wl = synth.small_workload(batch=4, tq=2, len_lo=2, len_hi=900, seed=161)
     inp = make(wl)
@@ -389,7 +427,9 @@ def test_clocked_decode_matches_and_reports_a_clock():
     clk = torch.zeros(2, dtype=torch.int64, device="cuda")
     api.decode_paged_clocked(q_lat, dev.q_r, dev.kv, dev.table, dev.lens, wl.scale, 3, po2, pl2, clk)
     torch.cuda.synchronize()
-    assert torch.equal(po, po2) and torch.equal(pl, pl2)
+    assert torch.equal(pl, pl2)
+    used = torch.isfinite(pl)
+    assert int(used.sum()) > 0 and torch.equal(po[used], po2[used])
     cyc, ticks = (int(v) for v in clk.cpu())
     assert cyc > 0 and ticks > 0
     assert 0.1 < 0.1 * cyc / ticks < 3.0
