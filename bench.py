@@ -252,8 +252,9 @@ def bench_prefill(steps, warmup):
 
 
 def bench_decode_configs(steps, warmup):
-    """The other decode workloads (single sequence, batched ragged, two-token
-    MTP verify, long context): one full step each (absorb, split-KV attention,
+    """The other decode workloads (single sequence, batched ragged, two-,
+    five- and eight-token verify, long context): one full step each (absorb,
+    split-KV attention,
     combine), cold-timed, placed against its binding roofline by arithmetic
     intensity.  Algorithmic bytes: KV rows + W_UK + W_UV + queries + outputs;
     FLOP: attention over every (query, visible key) pair + absorb + W_UV."""
@@ -264,7 +265,7 @@ def bench_decode_configs(steps, warmup):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     res = {}
-    for name in ("single", "batched", "mtp", "long"):
+    for name in ("single", "batched", "mtp", "verify5", "verify8", "long"):
         wl = synth.WORKLOADS[name]
         inp = synth.make_inputs(wl)
         B, Tq = wl.batch, wl.tq

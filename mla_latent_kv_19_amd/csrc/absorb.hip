@@ -10,18 +10,31 @@
 // slice of W_UK once in LDS, keeps it in registers as the A operand of
 // q_lat^T = W_UK[h]^T . q_C^T (transposed LDS reads give the 8-consecutive-i
 // operand layout), and streams all query rows through it in blocks of 32.
+//
+// Every global access is a whole row piece: a query row q_C[m, h, :] is 256
+// contiguous bytes, read by 16 lanes, and the block's 256-byte piece of a
+// q_lat row likewise; both pass through LDS to and from the MFMA layouts
+// (lane = row, 8 consecutive values), which read or write only 32 bytes of a
+// row per lane pair and would touch 32 cache lines per instruction.  The rows
+// of 128 queries (four blocks) are loaded in one round trip, 32 bytes of
+// registers per row and lane group.
 #include "mla_common.h"
 
 namespace mla {
 
 constexpr int kAbsThreads = 256;
-constexpr int kAbsPitch = 128 + 32;   // bf16 per LDS row (320 B: rows 16 banks apart, so the
+constexpr int kAbsPitch = 128 + 32;   // bf16 per W LDS row (320 B: rows 16 banks apart, so the
                                       // 4 rows of a transposed read hit disjoint banks)
+constexpr int kRowPitch = 128 + 8;    // bf16 per query / output LDS row (272 B: 16 consecutive
+                                      // rows read at one column hit 16 distinct 4-bank groups)
+constexpr int kGroupRows = 128;       // query rows in flight together
 
 __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_c,
                                                                const uint16_t* __restrict__ w_uk,
                                                                uint16_t* __restrict__ q_lat, int M) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[128 * kAbsPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kRowPitch];   // one block of query rows
+  __shared__ __attribute__((aligned(16))) uint16_t os[32 * kRowPitch];   // one block of q_lat pieces
   const int h = blockIdx.x >> 2;
   const int jblk = blockIdx.x & 3;
   const int tid = threadIdx.x;
@@ -30,23 +43,29 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* _
   const int l32 = lane & 31;
   const int wave = tid >> 6;
 
-  // Query operands of a block of 32 rows (lane: row m0 + l32, 8 consecutive i).
-  // q_c through an empty asm: loads from a const __restrict__ argument count as
-  // invariant, and the compiler then sinks the first block's loads past the
-  // weight staging below (to their first use), serialising the two round trips.
-  typedef __attribute__((address_space(1))) const bf16x8 gbl_bf16x8;
+  // Query rows g0 .. g0+127 (clamped to M - 1): thread tid holds 16-byte
+  // chunk tid % 16 of rows g0 + 16 k + tid / 16, k = 0..7; block b of 32 rows
+  // is in k = 2b, 2b + 1.  q_c through an empty asm: loads from a const
+  // __restrict__ argument count as invariant, and the compiler then sinks the
+  // first group's loads past the weight staging below (to their first use),
+  // serialising the two round trips.
   const uint16_t* q_src = q_c;
   asm volatile("" : "+s"(q_src));
-  auto load_q = [&](int m0, bf16x8 (&bq)[8]) {
-    const int m = m0 + l32;
-    const uint16_t* src = q_src + ((size_t)min(m, M - 1) * 128 + h) * 128 + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bq[ks] = *(gbl_bf16x8*)(src + 16 * ks);
+  const int rc = tid & 15, rr = tid >> 4;
+  // Named chunks, not an array: an array indexed by the block loop is kept in
+  // scratch memory.
+  struct QRows {
+    uint4 k0, k1, k2, k3, k4, k5, k6, k7;
+  } qv;
+  auto q_chunk = [&](int g0, int k) {
+    const int m = min(g0 + 16 * k + rr, M - 1);
+    return *reinterpret_cast<const uint4*>(q_src + ((size_t)m * 128 + h) * 128 + rc * 8);
   };
-  // The first block's queries are loaded before the weight slice is staged, so
-  // the two loads overlap.
-  bf16x8 bq[8];
-  load_q(0, bq);
+  auto load_group = [&](int g0) {
+    qv.k0 = q_chunk(g0, 0); qv.k1 = q_chunk(g0, 1); qv.k2 = q_chunk(g0, 2); qv.k3 = q_chunk(g0, 3);
+    qv.k4 = q_chunk(g0, 4); qv.k5 = q_chunk(g0, 5); qv.k6 = q_chunk(g0, 6); qv.k7 = q_chunk(g0, 7);
+  };
+  load_group(0);
 
   // Stage W_UK[h][0:128][128*jblk : +128]: 128 rows x 256 B = 2048 16-byte chunks.
   const uint16_t* wsrc = w_uk + (size_t)h * 128 * 512 + jblk * 128;
@@ -74,27 +93,44 @@ __global__ __launch_bounds__(kAbsThreads) void absorb_q_kernel(const uint16_t* _
     a[ks] = cat(lo, hi);
   }
 
-  for (int m0 = 0; m0 < M; m0 += 32) {
-    // Next block's queries in flight during this block's product.
-    bf16x8 bn[8];
-    if (m0 + 32 < M) load_q(m0 + 32, bn);
-    f32x16 acc = {};
+  for (int g0 = 0; g0 < M; g0 += kGroupRows) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
-    // acc[r]: j = 32*wave + 8*(r/4) + 4*half + r%4, m = m0 + l32.
-    const int m = m0 + l32;
-    if (m < M) {
-      uint16_t* dst = q_lat + ((size_t)m * 128 + h) * 512 + jblk * 128 + 32 * wave + 4 * half;
+    for (int bk = 0; bk < kGroupRows / 32; ++bk) {
+      const int m0 = g0 + 32 * bk;
+      if (m0 >= M) continue;                           // uniform: every thread skips
+      // The block's query rows into LDS (the previous block's operand reads
+      // and output reads are done: the barrier at the end of its iteration).
+      const uint4 lo = bk == 0 ? qv.k0 : bk == 1 ? qv.k2 : bk == 2 ? qv.k4 : qv.k6;
+      const uint4 hi = bk == 0 ? qv.k1 : bk == 1 ? qv.k3 : bk == 2 ? qv.k5 : qv.k7;
+      *reinterpret_cast<uint4*>(&qs[rr * kRowPitch + rc * 8]) = lo;
+      *reinterpret_cast<uint4*>(&qs[(16 + rr) * kRowPitch + rc * 8]) = hi;
+      __syncthreads();
+      // B operands: lane = row l32, i = 16 ks + 8 half .. +7.
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma32(a[ks], *reinterpret_cast<const bf16x8*>(&qs[l32 * kRowPitch + 16 * ks + 8 * half]), acc);
+      // acc[r]: j = 32*wave + 8*(r/4) + 4*half + r%4 (of the block's 128), m = m0 + l32.
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)acc[4 * g + e];
-        *reinterpret_cast<bf16x4*>(dst + 8 * g) = v;
+        *reinterpret_cast<bf16x4*>(&os[l32 * kRowPitch + 32 * wave + 8 * g + 4 * half]) = v;
       }
-    }
+      __syncthreads();
+      // Row pieces out: thread tid writes chunk tid % 16 of rows tid / 16 and
+      // 16 + tid / 16.
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bq[ks] = bn[ks];
+      for (int k = 0; k < 2; ++k) {
+        const int r = 16 * k + rr, m = m0 + r;
+        if (m < M)
+          *reinterpret_cast<uint4*>(q_lat + ((size_t)m * 128 + h) * 512 + jblk * 128 + rc * 8) =
+              *reinterpret_cast<const uint4*>(&os[r * kRowPitch + rc * 8]);
+      }
+      __syncthreads();
+    }
+    if (g0 + kGroupRows < M) load_group(g0 + kGroupRows);
   }
 }
 

@@ -112,6 +112,12 @@ WORKLOADS = {
                         note="causal prefill, T=4096"),
     "headline": Workload("headline", batch=64, tq=1, len_lo=32768, len_hi=32768, seed=1006,
                          note="B=64 paged decode, L=32,768"),
+    # Wider speculative verification: a token plus 4 or 7 drafts per sequence,
+    # the MTP workload's batch and lengths otherwise.
+    "verify5": Workload("verify5", batch=64, tq=5, len_lo=4096, len_hi=8192, seed=1007,
+                        note="B=64 five-query causal verify, L ~ U[4096, 8192]"),
+    "verify8": Workload("verify8", batch=64, tq=8, len_lo=4096, len_hi=8192, seed=1008,
+                        note="B=64 eight-query causal verify, L ~ U[4096, 8192]"),
 }
 
 

@@ -323,6 +323,12 @@ def test_workload_mtp_sampled():
     _sampled_full_size("mtp")
 
 
+@pytest.mark.parametrize("name", ["verify5", "verify8"])
+def test_workload_verify_sampled(name):
+    print(f"[case] workload {name}", flush=True)
+    _sampled_full_size(name, n_picks=2)
+
+
 def test_workload_long_sampled():
     print("[case] workload long", flush=True)
     _sampled_full_size("long", n_picks=2)

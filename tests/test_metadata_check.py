@@ -25,7 +25,7 @@ def test_valid_metadata_passes():
 def test_seeded_workloads_pass():
     """The generator's block tables (a seeded permutation of the pool, one
     owner per block) meet every precondition at the bench and parity shapes."""
-    for name in ("single", "batched", "mtp", "long", "headline", "prefill"):
+    for name in ("single", "batched", "mtp", "verify5", "verify8", "long", "headline", "prefill"):
         wl = synth.WORKLOADS[name]
         lens = synth.seq_lens_for(wl)
         table, num_blocks = synth.block_table_for(wl, lens)

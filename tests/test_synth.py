@@ -88,6 +88,7 @@ def test_named_workloads():
     w = synth.WORKLOADS
     assert (w["headline"].batch, w["headline"].len_lo, w["headline"].tq) == (64, 32768, 1)
     assert (w["mtp"].tq, w["mtp"].len_lo, w["mtp"].len_hi) == (2, 4096, 8192)
+    assert (w["verify5"].tq, w["verify8"].tq, w["verify8"].batch) == (5, 8, 64)
     assert w["long"].len_lo == 163840
     assert w["prefill"].tq == w["prefill"].len_lo == 4096
     assert w["single"].scale == pytest.approx(192 ** -0.5)
