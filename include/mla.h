@@ -124,8 +124,9 @@ int mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_lat,
  *   planned on the device from seq_lens: the sequences' blocks are laid end
  *   to end (each sequence charged 6 blocks more for its fixed per-split cost,
  *   unless all sequences have the same block count) and cut into equal
- *   chunks, as many as the device holds work-groups at once (its compute
- *   units / Tq, at most B * S), but no shorter than ceil(longest / (S - 1))
+ *   chunks, as many as the device holds work-groups at once (XCDs x
+ *   floor(compute units per XCD / Tq), at most B * S), but no shorter than
+ *   ceil(longest / (S - 1))
  *   blocks, so that each sequence meets at most S chunks.  Sequence b's part
  *   of chunk u goes to slot u - (chunk of its first block); its slots past
  *   the last are empty.

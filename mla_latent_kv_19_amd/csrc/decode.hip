@@ -669,22 +669,29 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
   }
 }
 
-// Compute units of the current device (cached per device).
-hipError_t device_cu_count(int* cus) {
+// Compute units and accelerator complex dies (XCDs) of the current device,
+// cached per device.  Consecutive work-group ids go to different XCDs.
+hipError_t device_cu_count(int* cus, int* xcds) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];
+  static std::atomic<int> cached_cus[kMaxDevices], cached_xcds[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
+  int n = cached_cus[dev].load(std::memory_order_relaxed);
+  int x = cached_xcds[dev].load(std::memory_order_relaxed);
+  if (n <= 0 || x <= 0) {
     e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (n <= 0) return hipErrorInvalidDevice;
-    cached[dev].store(n, std::memory_order_relaxed);
+    if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0 ||
+        n % x != 0)
+      x = 1;
+    cached_cus[dev].store(n, std::memory_order_relaxed);
+    cached_xcds[dev].store(x, std::memory_order_relaxed);
   }
   *cus = n;
+  *xcds = x;
   return hipSuccess;
 }
 
@@ -701,16 +708,21 @@ extern "C" hipError_t mla_launch_decode_paged(
   // One slot per sequence: one unit per sequence (plan 0).  Fewer than 64
   // query rows: one unit per (sequence, split) (plan 1, no scan of the
   // lengths: the lowest start-up latency).  Otherwise the token-balanced plan
-  // 2 with as many units as the chip holds work-groups at once (one per
-  // compute unit; Tq per unit), but no more than B * num_splits, the most
-  // pieces the slots can take (the plan's chunk length adapts to the count).
+  // 2 with as many units as the chip holds work-groups at once, but no more
+  // than B * num_splits, the most pieces the slots can take (the plan's chunk
+  // length adapts to the count).  Work-group ids go round-robin over the
+  // XCDs and the Tq work-groups of a unit share one, so each XCD gets
+  // floor(its compute units / Tq) units: with cus / Tq units, for Tq = 5 on
+  // 8 XCDs of 32, three would get 35 work-groups and run a second round.
   int plan = (num_splits == 1) ? 0 : ((long)B * Tq < mla::kBalanceMinRows ? 1 : 2);
   int num_units = (plan == 1) ? B * num_splits : B;
   if (plan == 2) {
-    int cus = 0;
-    const hipError_t e = mla::device_cu_count(&cus);
+    int cus = 0, xcds = 1;
+    const hipError_t e = mla::device_cu_count(&cus, &xcds);
     if (e != hipSuccess) return e;
-    num_units = static_cast<int>(std::max(1L, std::min((long)cus / Tq, (long)B * num_splits)));
+    const long per_xcd = cus / xcds;
+    const long resident = per_xcd >= Tq ? xcds * (per_xcd / Tq) : cus / Tq;
+    num_units = static_cast<int>(std::max(1L, std::min(resident, (long)B * num_splits)));
   }
   const int grid = ((num_units + 7) / 8) * 8 * Tq;
   float scale_log2 = softmax_scale * mla::kLog2e;
