@@ -60,9 +60,11 @@ constexpr int kRing = 4;                        // stages in the LDS ring
 constexpr int kLoadsPerThread = kTileBytes / 16 / kDecThreads;  // 9
 constexpr int kQrBytes = 128 * 64 * 2;          // rotary queries of the 128 heads
 constexpr int kDecLdsBytes = kRing * kTileBytes + kQrBytes;      // 163840
+constexpr int kQStageBytes = 32 * 512;          // one wave's half query rows (start-up staging)
 
 static_assert(kLoadsPerThread * 16 * kDecThreads == kTileBytes, "tile must split evenly");
 static_assert(kDecLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(4 * kQStageBytes <= 2 * kTileBytes, "query staging inside stages 2 and 3");
 static_assert(4 * 32 * (256 + 4) * 4 <= kRing * kTileBytes, "epilogue transpose area inside the ring");
 
 // Lazy renormalisation threshold (log2 units): unnormalised weights stay <= 2^8.
@@ -124,6 +126,20 @@ __device__ __forceinline__ void load_piece(const char* gw, int voff, lds_u8* sta
   asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%4"
                :
                : "v"(voff), "s"(sb), "s"(m0), "n"(IT * (kBlkBytes - 128)), "n"(IT * 128)
+               : "m0");
+}
+// One 16-byte direct-to-LDS load per lane: lane j's bytes land at
+// dst + 16 j; the source is sbase + voff (sbase wave-uniform, voff per lane).
+__device__ __forceinline__ void dma16(const char* sbase, unsigned voff, lds_u8* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>(dst)));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(sbase);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(a >> 32));
+  const unsigned long long sb = (static_cast<unsigned long long>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sb), "s"(m0)
                : "m0");
 }
 // Piece `it` (a compile-time constant at every call site once unrolled).
@@ -246,18 +262,44 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       return kv + ((size_t)table[t >> 6] * kTok + (t & (kTok - 1))) * kRowVals;
     };
 
-    // Start-up loads, in this order so that one round trip brings what the first
-    // score product needs: the latent queries (registers), tile 0, the rotary
-    // queries (staged in LDS: waiting for them also waits for everything issued
-    // before, vmcnt being in order), then tile 1, which streams in behind.
-    // Latent queries as B operands: k-step kk covers dims 16kk .. 16kk+15.
+    // Start-up loads.  The latent queries (B operands: k-step kk covers dims
+    // 16kk .. 16kk+15, lane = head) are staged through LDS as whole row pieces:
+    // loaded straight into registers, every instruction would read 32 bytes
+    // from each of 32 head rows (32 cache lines), and the 128 KB of queries
+    // took ~1k line requests per wave.  Stages 2 and 3 of the ring are free
+    // until tile 2's loads (after the first tile barrier), room for half the
+    // queries: round 0 brings dims 0..255 of the wave's 32 rows, round 1 dims
+    // 256..511, each 16 direct-to-LDS loads of two 512-byte row halves, their
+    // 16-byte chunks XOR-swizzled by the row's low 4 bits (the operand reads,
+    // 16 rows at one chunk, then hit distinct banks).  Order: round 0, tile 0,
+    // the rotary queries (registers -> LDS), round 0 read out, then round 1 and
+    // tile 1 together; the first tile's wait covers round 1, which is read out
+    // before its barrier (tile 2's loads overwrite the staging area after it).
     bf16x8 qreg[32];
-    {
-      const uint16_t* ql = q_lat + qrow * 512;
-      const unsigned q_off = static_cast<unsigned>(head * 512 + 8 * half);
+    lds_u8* q_stage = smem + 2 * kTileBytes + wave * kQStageBytes;
+    const char* q_rows = reinterpret_cast<const char*>(q_lat + (qrow + 32 * wave) * 512);
+    // The per-lane source offsets depend only on the lane: computed from a
+    // register the compiler cannot see is the lane id, so that they are not
+    // hoisted out of the loop over pieces and kept alive (spilled) across it.
+    auto issue_q_round = [&](int rnd) {
+      int ln;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) qreg[kk] = ld_global_bf16x8(ql + q_off + 16 * kk);
-    }
+      for (int j = 0; j < 16; ++j) {
+        const int r = 2 * j + (ln >> 5);                  // row of this lane's chunk
+        const int c = (ln & 31) ^ (r & 15);               // source chunk of LDS slot ln & 31
+        dma16(q_rows, static_cast<unsigned>(r * 1024 + rnd * 512 + c * 16), q_stage + j * 1024);
+      }
+    };
+    auto read_q_round = [&](int rnd) {
+      int ln;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane) : "memory");
+      const int r = ln & 31, h = ln >> 5;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        qreg[16 * rnd + k] = ld_lds_bf16x8(q_stage + r * 512 + (((2 * k + h) ^ (r & 15)) * 16));
+    };
+    issue_q_round(0);
 
     {
       const char* g0 = reinterpret_cast<const char*>(tile_rows(0)) + wave * 8 * kRowBytes;
@@ -274,6 +316,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       const uint4 v = *reinterpret_cast<const uint4*>(q_r + (qrow + h) * 64 + c * 8);
       st_lds16(qr_lds + (h * 8 + (c ^ ((h >> 1) & 7))) * 16, v);
     }
+
+    // Round 0 has landed (it precedes everything still outstanding): read it
+    // out, then refill the staging area with round 1.
+    wait_vmcnt<0>();
+    read_q_round(0);
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    issue_q_round(1);
 
     if (ntiles > 1) {
       const char* g1 = reinterpret_cast<const char*>(tile_rows(1)) + wave * 8 * kRowBytes;
@@ -322,13 +372,16 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
       const char* g;       // this wave's row group of tile n+2, or null
       lds_u8* stage;       // its LDS destination
     };
-    auto top = [&](int n, Next& nx) {
+    auto top = [&](auto FIRST, int n, Next& nx) {
       // Page of tile n+2: a scalar load issued now, so that the wait of the
       // barrier below covers it (issued after the barrier, its wait stalled the
       // start of the score product of every wave).
       const int pg2 = (n + 2 < ntiles) ? table[(T0 + (n + 2) * kTileTok) >> 6] : 0;
       // This wave's rows of tile n have landed (its own direct-to-LDS loads).
       if (n + 1 < ntiles) wait_vmcnt<kLoadsPerThread>(); else wait_vmcnt<0>();
+      // First tile: query round 1 (issued before tile 1) has landed too; read
+      // it out before the barrier, after which tile 2 overwrites the area.
+      if constexpr (decltype(FIRST)::value) read_q_round(1);
       const int valid = L - (T0 + n * kTileTok);        // rows of tile n inside the sequence
       if (valid < 8 * wave + 8) {
         // Rows past the sequence end may hold anything (NaN): each wave zeroes
@@ -490,7 +543,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     {
       f32x16 s0;
       Next nx;
-      top(0, nx);
+      top(std::true_type{}, 0, nx);
       scores(std::false_type{}, 0, nx, s0);
       Softmax st;
 #pragma unroll
@@ -505,7 +558,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     int n = 1;
     for (; n < n_ld; ++n) {
       Next nx;
-      top(n, nx);
+      top(std::false_type{}, n, nx);
       f32x16 sn;
       scores(std::true_type{}, n, nx, sn);
       bf16x8 pb2[2];
@@ -519,7 +572,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_paged_kernel(
     }
     for (; n < ntiles; ++n) {
       Next nx;
-      top(n, nx);
+      top(std::false_type{}, n, nx);
       f32x16 sn;
       scores(std::false_type{}, n, nx, sn);
       bf16x8 pb2[2];
