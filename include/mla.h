@@ -78,8 +78,9 @@ enum {
 #define MLA_MAX_SPLITS 256
 
 /* Most (split, query row) pairs, num_splits * B * Tq, that mla_decode_noalloc
- * keeps in its library-owned buffer (64 MiB + 128 KiB per GPU). */
-#define MLA_NOALLOC_MAX_PAIRS 256
+ * keeps in its library-owned buffer (160 MiB + 320 KiB per GPU: a decode step of
+ * 64 sequences with the 9 slots mla_decode_num_splits suggests fits). */
+#define MLA_NOALLOC_MAX_PAIRS 640
 
 /* Static string describing a status code (never NULL). */
 const char* mla_strerror(int status);
@@ -174,8 +175,8 @@ int mla_combine(const float* part_o, const float* part_lse, const uint16_t* w_uv
  * mla_decode_paged followed by one mla_combine (same kernels, same results
  * bit for bit), with part_o and part_lse kept in a buffer the library owns
  * instead of caller workspace.  Allocates nothing: the buffer is a static
- * device array of MLA_NOALLOC_MAX_PAIRS (split, query row) pairs, 64 MiB +
- * 128 KiB, one per GPU the library runs on, held until the process ends; its
+ * device array of MLA_NOALLOC_MAX_PAIRS (split, query row) pairs, 160 MiB +
+ * 320 KiB, one per GPU the library runs on, held until the process ends; its
  * device address is looked up once per device on the first call there.
  * Arguments as for mla_decode_paged and mla_combine (out bf16 [B, Tq, H, d_v],
  * lse_out fp32 [B, Tq, H] or NULL).  Every call on one GPU shares that GPU's

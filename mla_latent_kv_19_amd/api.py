@@ -21,7 +21,7 @@ _lib = None
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_ERR_NOALLOC_LIMIT = 4
 MLA_MAX_SPLITS = 256
-MLA_NOALLOC_MAX_PAIRS = 256
+MLA_NOALLOC_MAX_PAIRS = 640
 
 # Shapes the kernels are written for.
 H, D_C, D_R, D_H, D_V, BLOCK = 128, 512, 64, 128, 128, 64

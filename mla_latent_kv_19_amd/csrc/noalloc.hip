@@ -44,7 +44,7 @@ constexpr int kMaxDevices = 64;
 
 }  // namespace
 
-// 64 MiB of partial outputs followed by 128 KiB of log-sum-exps.
+// 160 MiB of partial outputs followed by 320 KiB of log-sum-exps.
 static __device__ __align__(256) float scratch[kPartOFloats + kPartLseFloats];
 
 namespace {

@@ -265,8 +265,8 @@ def test_noalloc_argument_errors():
     assert call(kv=NULL) == api.MLA_ERR_INVALID_ARG
     assert call(splits=0) == api.MLA_ERR_INVALID_ARG
     assert call(H=64) == api.MLA_ERR_UNSUPPORTED
-    assert call(B=64, splits=5) == api.MLA_ERR_NOALLOC_LIMIT       # 320 pairs
-    assert call(B=65, Tq=2, splits=2) == api.MLA_ERR_NOALLOC_LIMIT
+    assert call(B=64, splits=11) == api.MLA_ERR_NOALLOC_LIMIT      # 704 pairs
+    assert call(B=65, Tq=2, splits=5) == api.MLA_ERR_NOALLOC_LIMIT  # 650 pairs
     assert b"NOALLOC_LIMIT" in lib.mla_strerror(api.MLA_ERR_NOALLOC_LIMIT)
 
 

@@ -33,7 +33,7 @@ def _noalloc_path(dev, q_lat, splits):
 
 @pytest.mark.parametrize("first,second", [
     ((16, 2, 1, 1500, 8), (3, 1, 1, 200, 3)),       # (batch, tq, len_lo, len_hi, splits)
-    ((64, 1, 1, 2048, 4), (5, 2, 2, 700, 16)),      # the buffer's full size, then a smaller call
+    ((64, 1, 1, 2048, 10), (5, 2, 2, 700, 16)),     # the buffer's full size (640 pairs), then a smaller call
 ])
 def test_noalloc_matches_workspace_path(first, second):
     for k, (batch, tq, lo, hi, splits) in enumerate((first, second)):
@@ -61,4 +61,4 @@ def test_noalloc_limit_is_rejected():
     q_lat = api.absorb_q(dev.q_c, dev.w_uk)
     out = torch.empty((65, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(api.MLAError, match="NOALLOC_LIMIT"):
-        api.decode_noalloc(q_lat, dev.q_r, dev.kv, dev.table, dev.lens, dev.w_uv, wl.scale, 4, out)
+        api.decode_noalloc(q_lat, dev.q_r, dev.kv, dev.table, dev.lens, dev.w_uv, wl.scale, 10, out)
