@@ -14,23 +14,45 @@
 // matrix work.  W_UV[h] is staged through LDS in 128-row slices and read with
 // transposed reads to form the 8-consecutive-j operand layout.  The split merge
 // skips row groups that lie past M; when a block holds at most eight rows, the
-// two halves of the work-group take alternate splits of the same rows and add
-// their fp32 partial sums in LDS, so few-row decode does not leave half idle.
+// row groups of the work-group take alternate splits of the same rows and add
+// their fp32 partial sums in LDS, so few-row decode does not leave them idle.
+//
+// Two forms.  Up to 64 rows (at most 256 work-groups: one round on the chip)
+// the merge covers all 512 latent columns at once (~109 KB of LDS, one
+// work-group per compute unit).  Past that the work-group runs two passes of
+// 256 columns (merge, then the matching 256 rows of W_UV), ~78 KB of LDS, so
+// that two share a compute unit and one's memory round trips overlap the
+// other's work: 128 rows 30 -> 24 us, 512 rows 80 -> 55 us; at 32 rows and
+// fewer the single pass is 1-2 us faster.
 #include "mla_common.h"
 
 namespace mla {
 
 constexpr int kCmbThreads = 256;
-constexpr int kOPitch = 512 + 8;     // bf16 per o_lat LDS row (1040 B)
 constexpr int kWPitch = 128 + 32;    // bf16 per W_UV LDS row (320 B: rows 16 banks apart,
                                      // so the 4 rows of a transposed read hit disjoint banks)
 constexpr int kLseLoads = 5;         // split log-sum-exps per thread in the first round trip
 constexpr int kWtsMin = kLseLoads * kCmbThreads;   // weight slots always present (40 splits)
 
+// LDS of one form: merged rows (hi and lo), one W_UV slice, split weights.
+constexpr size_t combine_lds(int passes, int S) {
+  return (size_t)(2 * 32 * (512 / passes + 8) + 128 * kWPitch) * 2 +
+         (size_t)(S * 32 > kWtsMin ? S * 32 : kWtsMin) * 4 + 16;
+}
+static_assert(combine_lds(2, 40) <= 80 * 1024, "two-pass form: two work-groups per compute unit");
+
+template <int kPasses>
 __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ lse_out,
     int M, int S) {
+  constexpr int kOCols = 512 / kPasses;              // latent columns per pass
+  constexpr int kOPitch = kOCols + 8;                // bf16 per o_lat LDS row
+  constexpr int kRowLanes = kOCols / 4;              // threads per merged row (4 columns each)
+  constexpr int kGroups = kCmbThreads / kRowLanes;   // groups of eight rows merged at once
+  constexpr int kIters = 32 / (8 * kGroups);         // rounds of row groups per pass
+  constexpr int kSlices = 4 / kPasses;               // W_UV slices per pass
+  static_assert(kGroups * 8 * kOCols * 4 <= 128 * kWPitch * 2, "pair-form scratch inside the W_UV area");
   extern __shared__ __attribute__((aligned(16))) unsigned char cmb_smem[];
   uint16_t* o_hi = reinterpret_cast<uint16_t*>(cmb_smem);             // [32][kOPitch]
   uint16_t* o_lo = o_hi + 32 * kOPitch;                               // [32][kOPitch]
@@ -91,6 +113,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
   }
   load_w(0, w0);
+  if constexpr (kPasses == 2) load_w(1, w1);
 #pragma unroll
   for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
@@ -127,39 +150,40 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   }
   __syncthreads();
 
-  // 2. o_lat rows: thread handles columns 4*(tid%128) .. +3 of eight
-  // consecutive rows, r0 .. r0+7 with r0 = 8*(tid/128) (+16 in the second
-  // iteration), so that the partials of eight rows and two splits are in flight
-  // together.  A group of eight rows with none below M is skipped (uniform per
-  // pair of waves): its LDS rows only feed output rows >= M, which are never
-  // written.  When the block has at most eight rows below M, both pairs of
-  // waves work on them, each on every second split, and their fp32 sums meet
-  // in the (not yet used) W_UV staging area.  Splits past the block's last
-  // one of non-zero weight are not visited; a split of weight 0 before it
-  // (empty: lse = -inf, its partial never written) is read and dropped by a
-  // select, not a branch, which keeps the loads of eight rows and two splits
-  // in flight together (reading split 0's row in its place, or testing the
-  // weight first, measured slower).
-  {
-    const int cq = tid & 127, hh = tid >> 7;
-    const bool pair = M - m0 <= 8;                      // uniform over the work-group
-    float* scratch = reinterpret_cast<float*>(wt);      // [2][8][512] when pair
-    auto store_hilo = [&](int r, float4 v) {
-      const float ov[4] = {v.x, v.y, v.z, v.w};
-      bf16x4 hi, lo;
+  // 2. o_lat rows, pass p: columns kOCols p .. +kOCols-1.  Thread handles
+  // columns 4*(tid % kRowLanes) .. +3 (a row's pass columns are one contiguous
+  // read across kRowLanes threads) of eight consecutive rows, r0 .. r0+7 with
+  // r0 = 8*(tid / kRowLanes) (+8 kGroups in later rounds), so that the
+  // partials of eight rows and two splits are in flight together.  A group of
+  // eight rows with none below M is skipped (uniform per row group): its LDS
+  // rows only feed output rows >= M, which are never written.  When the block
+  // has at most eight rows below M, every row group works on them, each on
+  // every kGroups-th split, and their fp32 sums meet in the (then unused) W_UV
+  // staging area.  Splits past the block's last one of non-zero weight are not
+  // visited; a split of weight 0 before it (empty: lse = -inf, its partial
+  // never written) is read and dropped by a select, not a branch, which keeps
+  // the loads of eight rows and two splits in flight together (reading split
+  // 0's row in its place, or testing the weight first, measured slower).
+  const int cq = tid % kRowLanes, grp = tid / kRowLanes;
+  const bool pair = M - m0 <= 8;                      // uniform over the work-group
+  float* scratch = reinterpret_cast<float*>(wt);      // [kGroups][8][kOCols] when pair
+  auto store_hilo = [&](int r, float4 v) {
+    const float ov[4] = {v.x, v.y, v.z, v.w};
+    bf16x4 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = (__bf16)ov[e];
-        lo[e] = (__bf16)(ov[e] - (float)hi[e]);
-      }
-      *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
-      *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
-    };
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (__bf16)ov[e];
+      lo[e] = (__bf16)(ov[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<bf16x4*>(&o_hi[r * kOPitch + 4 * cq]) = hi;
+    *reinterpret_cast<bf16x4*>(&o_lo[r * kOPitch + 4 * cq]) = lo;
+  };
+  auto merge = [&](int p) {
 #pragma unroll 1
-    for (int it = 0; it < 2; ++it) {
-      const int r0 = pair ? 0 : hh * 8 + 16 * it;
+    for (int it = 0; it < kIters; ++it) {
+      const int r0 = pair ? 0 : grp * 8 + 8 * kGroups * it;
       if (pair ? it > 0 : m0 + r0 >= M) continue;
-      const int s_first = pair ? hh : 0, s_step = pair ? 2 : 1;
+      const int s_first = pair ? grp : 0, s_step = pair ? kGroups : 1;
       const int s_stop = *s_end_lds;
       float4 o[8];
 #pragma unroll
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
         for (int u = 0; u < 8; ++u) {
           const int m = min(m0 + r0 + u, M - 1);
           v[u] = *reinterpret_cast<const float4*>(part_o + (s * split_stride + (size_t)m * 128 + h) * 512 +
-                                                  4 * cq);
+                                                  kOCols * p + 4 * cq);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -186,24 +210,30 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
       if (pair) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          *reinterpret_cast<float4*>(&scratch[(hh * 8 + u) * 512 + 4 * cq]) = o[u];
+          *reinterpret_cast<float4*>(&scratch[(grp * 8 + u) * kOCols + 4 * cq]) = o[u];
       } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) store_hilo(r0 + u, o[u]);
       }
     }
+    // The pass's merged rows are in LDS for every wave (with few rows, after
+    // the row groups' sums are added).
     if (pair) {
       __syncthreads();
-      if (hh == 0) {
+      if (grp == 0) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float4 a0 = *reinterpret_cast<const float4*>(&scratch[u * 512 + 4 * cq]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&scratch[(8 + u) * 512 + 4 * cq]);
-          store_hilo(u, make_float4(a0.x + a1.x, a0.y + a1.y, a0.z + a1.z, a0.w + a1.w));
+          float4 a = *reinterpret_cast<const float4*>(&scratch[u * kOCols + 4 * cq]);
+#pragma unroll
+          for (int g2 = 1; g2 < kGroups; ++g2) {
+            const float4 c = *reinterpret_cast<const float4*>(&scratch[(8 * g2 + u) * kOCols + 4 * cq]);
+            a = make_float4(a.x + c.x, a.y + c.y, a.z + c.z, a.w + c.w);
+          }
+          store_hilo(u, a);
         }
       }
     }
-  }
+  };
 
   // 3. out[32 rows x 128] = o_lat . W_UV[h]; wave w owns columns 32w .. 32w+31.
   const int q16 = lane & 15;
@@ -212,38 +242,67 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
                       ((8 * half + (q16 >> 2)) * kWPitch + 32 * wave + 16 * colhalf + 4 * (q16 & 3)) * 2;
   const lds_u8* ahb = to_lds(o_hi) + (l32 * kOPitch + 8 * half) * 2;
   const lds_u8* alb = to_lds(o_lo) + (l32 * kOPitch + 8 * half) * 2;
-  load_w(1, w1);
-  load_w(2, w2);
   f32x16 acc = {};
+  // Slice jc of W_UV[h] (in LDS) against its 128 columns of the pass's rows.
   auto product = [&](int jc) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x4 blo = ld_lds_tr(trb + (16 * ks) * kWPitch * 2);
       const bf16x4 bhi = ld_lds_tr(trb + (16 * ks + 4) * kWPitch * 2);
       const bf16x8 bw = cat(blo, bhi);
-      const int koff = (jc * 128 + 16 * ks) * 2;
+      const int koff = ((jc % kSlices) * 128 + 16 * ks) * 2;
       acc = mfma32(ld_lds_bf16x8(ahb + koff), bw, acc);
       acc = mfma32(ld_lds_bf16x8(alb + koff), bw, acc);
     }
   };
-  // Each slice: every wave is done with the previous one, then it goes to LDS.
-  __syncthreads();
-  store_w(w0);
-  __syncthreads();
-  load_w(3, w0);
-  product(0);
-  __syncthreads();
-  store_w(w1);
-  __syncthreads();
-  product(1);
-  __syncthreads();
-  store_w(w2);
-  __syncthreads();
-  product(2);
-  __syncthreads();
-  store_w(w0);
-  __syncthreads();
-  product(3);
+  // A slice goes to LDS once every wave is done with the previous one (and
+  // with a pair-form scratch there).
+  if constexpr (kPasses == 1) {
+    // Slices 0 (since step 1), 1 and 2 in registers, 3 once slice 0 is in LDS.
+    merge(0);
+    load_w(1, w1);
+    load_w(2, w2);
+    __syncthreads();
+    store_w(w0);
+    __syncthreads();
+    load_w(3, w0);
+    product(0);
+    __syncthreads();
+    store_w(w1);
+    __syncthreads();
+    product(1);
+    __syncthreads();
+    store_w(w2);
+    __syncthreads();
+    product(2);
+    __syncthreads();
+    store_w(w0);
+    __syncthreads();
+    product(3);
+  } else {
+    // Slices 0 and 1 in registers since step 1; 2 and 3 follow them.
+    merge(0);
+    __syncthreads();
+    store_w(w0);
+    __syncthreads();
+    load_w(2, w0);
+    product(0);
+    __syncthreads();
+    store_w(w1);
+    __syncthreads();
+    load_w(3, w1);
+    product(1);
+    __syncthreads();
+    merge(1);                       // overwrites the merged rows (and slice 1 with few rows)
+    __syncthreads();
+    store_w(w0);
+    __syncthreads();
+    product(2);
+    __syncthreads();
+    store_w(w1);
+    __syncthreads();
+    product(3);
+  }
   // acc[r]: row m0 + 8*(r/4) + 4*half + r%4, column 32*wave + l32.
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -255,22 +314,25 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   }
 }
 
-size_t combine_lds_bytes(int S) {
-  return (size_t)(2 * 32 * kOPitch + 128 * kWPitch) * 2 + (size_t)(S * 32 > kWtsMin ? S * 32 : kWtsMin) * 4 + 16;
-}
-
 }  // namespace mla
 
 extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_lse,
                                          const uint16_t* w_uv, uint16_t* out, float* lse_out, int M,
                                          int S, hipStream_t stream) {
-  const size_t lds = mla::combine_lds_bytes(S);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&mla::combine_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::combine_lds_bytes(256));
-  if (attr != hipSuccess) return attr;
+  static const hipError_t attr1 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&mla::combine_kernel<1>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::combine_lds(1, 256));
+  static const hipError_t attr2 = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&mla::combine_kernel<2>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)mla::combine_lds(2, 256));
+  if (attr1 != hipSuccess) return attr1;
+  if (attr2 != hipSuccess) return attr2;
+  // One form per call: a single pass while the grid fits one round of one
+  // work-group per compute unit (M <= 64), two passes beyond.
+  const int passes = M > 64 ? 2 : 1;
   const int grid = 128 * ((M + 31) / 32);
   void* args[] = {&part_o, &part_lse, &w_uv, &out, &lse_out, &M, &S};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&mla::combine_kernel), dim3(grid),
-                         dim3(mla::kCmbThreads), args, lds, stream);
+  const void* fn = passes == 2 ? reinterpret_cast<const void*>(&mla::combine_kernel<2>)
+                               : reinterpret_cast<const void*>(&mla::combine_kernel<1>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(mla::kCmbThreads), args, mla::combine_lds(passes, S), stream);
 }
