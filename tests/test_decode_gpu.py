@@ -124,16 +124,21 @@ def test_split_counts(splits):
     _check_decode(make(wl), splits=splits, what=f"splits={splits}")
 
 
-@pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5)])
+@pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5), (36, 2, 5),
+                                              (67, 1, 40), (33, 3, 41)])
 def test_combine_row_blocks(batch, tq, splits):
-    """The combine's row-block forms: 15 rows with 40 splits (more than the 32
-    split weights one pass holds, rows 8-14 past the eight-row pair form), 40
-    rows with 33 splits (a full 32-row block, then a block of eight rows that
-    both wave pairs share by split parity) and 9 rows with 5 splits (one row
-    past the pair form).  Against the absorbed fp64 form, which is pinned to the
-    un-absorbed oracle to 1e-12."""
+    """The combine's row-block forms.  Single pass (at most 64 rows): 15 rows
+    with 40 splits (rows 8-14 past the eight-row pair form), 40 rows with 33
+    splits (a full 32-row block, then a block of eight rows that both row groups
+    share by split parity) and 9 rows with 5 splits (one row past the pair
+    form).  Two passes (more than 64 rows): 72 rows with 5 splits (a last block
+    of eight rows that the four row groups share), 67 rows with 40 splits (the
+    most log-sum-exps the first round trip reads; a last block of three rows)
+    and 99 rows with 41 splits (one split past it).  Against the absorbed fp64
+    form, which is pinned to the un-absorbed oracle to 1e-12."""
     print(f"[case] combine rows={batch * tq} splits={splits}", flush=True)
-    wl = synth.small_workload(batch=batch, tq=tq, len_lo=tq, len_hi=1500, seed=80 + splits)
+    wl = synth.small_workload(batch=batch, tq=tq, len_lo=tq, len_hi=1500 if batch * tq <= 64 else 700,
+                              seed=80 + splits + batch)
     inp = make(wl)
     out, lse = run_decode(DevInputs(inp), splits=splits)
     ref, ref_lse = oracle_decode(inp, form="absorbed")
