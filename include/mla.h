@@ -313,7 +313,7 @@ size_t mla_prefill_workspace_bytes(long total_kv_tokens, int H, int d_h, int d_v
 
 /*
  * Suggested num_splits (partial slots) for a decode step.  With at least
- * two rounds of work-groups in whole sequences (B * Tq >= 2 num_cus), or
+ * four rounds of work-groups in whole sequences (B * Tq >= 4 num_cus), or
  * sequences of one block, it is 1.
  * Otherwise, with c = ceil(num_cus / (B * Tq)) splits per sequence (capped
  * at the longest sequence's block count) filling the compute units about

@@ -315,9 +315,12 @@ int mla_decode_num_splits(int B, int Tq, int H, int max_seq_len, int block_size,
   if (B <= 0 || Tq <= 0 || H <= 0 || max_seq_len <= 0 || block_size <= 0 || num_cus <= 0) return 0;
   const long groups = (long)B * (((long)Tq * H + 127) / 128);    // work-groups per unit of work
   const long pages = (max_seq_len + block_size - 1) / block_size;
-  // Two or more rounds of whole sequences fill the chip by themselves, and a
-  // single block cannot be cut.
-  if (groups >= 2L * num_cus || pages == 1) return 1;
+  // Four or more rounds of whole sequences balance by themselves (the
+  // hardware starts each as a compute unit frees up), and a single block
+  // cannot be cut.  With two rounds the token-balanced plan is faster: B = 64,
+  // Tq = 8, L ~ U[4096, 8192] on MI355X 0.811 ms per step with 3 slots against
+  // 0.878 ms whole.
+  if (groups >= 4L * num_cus || pages == 1) return 1;
   // c splits per sequence fill the chip about once.  Below 64 query rows the
   // decode cuts each sequence into num_splits equal ranges: c.  From 64 rows
   // on it balances the batch's tokens: 2c (room for sequences up to twice the

@@ -144,10 +144,13 @@ def test_workspace_sizes_and_split_heuristic():
     assert lib.mla_decode_num_splits(1, 1, 128, 1024, 64, 256) == 16
     assert lib.mla_decode_num_splits(4, 1, 128, 128, 64, 256) == 2
     assert lib.mla_decode_num_splits(64, 1, 128, 128, 64, 256) == 3
-    # One block, or two rounds of whole sequences: one slot.
+    # One block, or four rounds of whole sequences: one slot; two rounds are
+    # token-balanced with 2 * 1 + 1 slots.
     assert lib.mla_decode_num_splits(1, 1, 128, 1, 64, 256) == 1
-    assert lib.mla_decode_num_splits(512, 1, 128, 32768, 64, 256) == 1
-    assert lib.mla_decode_num_splits(256, 2, 128, 32768, 64, 256) == 1
+    assert lib.mla_decode_num_splits(1024, 1, 128, 32768, 64, 256) == 1
+    assert lib.mla_decode_num_splits(256, 4, 128, 32768, 64, 256) == 1
+    assert lib.mla_decode_num_splits(512, 1, 128, 32768, 64, 256) == 3
+    assert lib.mla_decode_num_splits(64, 8, 128, 8192, 64, 256) == 3
     assert lib.mla_decode_num_splits(0, 1, 128, 1, 64, 256) == 0
     # The cap.
     assert lib.mla_decode_num_splits(1, 1, 128, 1 << 24, 64, 8192) == 256
