@@ -176,20 +176,27 @@ def _balanced_lens(kind, tq, rng):
         return list(rng.integers(tq, 129, size=140))
     if kind == "equal_odd":       # equal lengths whose chunks straddle sequences
         return [65 * 64 - 3] * 7      # 65 blocks: odd, so chunks of 2 or 33 straddle
+    if kind == "one_long_wide":   # 65 sequences: the balanced plan (64+ query rows)
+        return [3000] + list(rng.integers(tq, 131, size=64))
+    if kind == "equal_wide":      # 16 x 4 query rows, equal odd lengths: balanced, no start-up cost
+        return [17 * 64 - 3] * 16
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("kind,tq,splits", [
     ("one_long", 1, None), ("one_long", 1, 2), ("one_long", 2, 3), ("two_steps", 2, None),
     ("two_steps", 3, 4), ("short", 1, None), ("short", 2, 2), ("equal_odd", 1, None),
-    ("equal_odd", 5, 3)])
+    ("equal_odd", 5, 3), ("one_long_wide", 1, None), ("one_long_wide", 1, 2),
+    ("equal_wide", 4, None), ("equal_wide", 4, 3)])
 def test_token_balanced_plan(kind, tq, splits):
-    """The device-side token-balanced split: chunks that straddle sequences,
-    units with several pieces, slot counts bound by num_splits (2 and 3 force
-    chunks of ceil(longest / (S - 1)) blocks), a scan over more than 64
-    sequences, and equal lengths (planned without the per-sequence cost).
-    Every query row against the absorbed fp64 form, which is pinned to the
-    un-absorbed oracle to 1e-12."""
+    """The split plans.  Token-balanced (64+ query rows: one_long with Tq = 2,
+    two_steps, short, one_long_wide, equal_wide): chunks that straddle
+    sequences, units with several pieces, slot counts bound by num_splits (2
+    and 3 force chunks of ceil(longest / (S - 1)) blocks), a scan over more
+    than 64 sequences, and equal lengths (planned without the per-sequence
+    cost, 17 blocks each so that chunks straddle).  Equal ranges per sequence
+    (fewer rows: one_long with Tq = 1, equal_odd).  Every query row against the
+    absorbed fp64 form, which is pinned to the un-absorbed oracle to 1e-12."""
     print(f"[case] balanced plan {kind} tq={tq} splits={splits}", flush=True)
     rng = np.random.default_rng(900 + tq)
     lens = _balanced_lens(kind, tq, rng)
