@@ -8,7 +8,8 @@
 // up-projection v = W_UV c folds into the output side, so
 //   out[m, h, d] = sum_j o_lat[m, h, j] W_UV[h][j][d]      (512 -> 128)
 //
-// One work-group per (head, block of 32 query rows).  The merged o_lat rows are
+// One work-group per (head, block of 32 query rows; 16 when there are at most
+// 32 rows, so that 17-32 rows still fill 256 work-groups).  The merged o_lat rows are
 // kept in LDS as a bf16 hi/lo pair (o = hi + lo to about 16 bits), so the
 // bf16 MFMA product carries nearly fp32 accuracy of o_lat at twice the (tiny)
 // matrix work.  W_UV[h] is staged through LDS in 128-row slices and read with
@@ -45,7 +46,7 @@ template <int kPasses>
 __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out, float* __restrict__ lse_out,
-    int M, int S) {
+    int M, int S, int rb) {
   constexpr int kOCols = 512 / kPasses;              // latent columns per pass
   constexpr int kOPitch = kOCols + 8;                // bf16 per o_lat LDS row
   constexpr int kRowLanes = kOCols / 4;              // threads per merged row (4 columns each)
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   int* s_end_lds = reinterpret_cast<int*>(wts + (S * 32 > kWtsMin ? S * 32 : kWtsMin));  // 1 + last split of weight > 0
 
   const int h = blockIdx.x % 128;
-  const int m0 = (blockIdx.x / 128) * 32;
+  const int m0 = (blockIdx.x / 128) * rb;
+  const int m_end = min(M, m0 + rb);             // rows of this block: m0 .. m_end-1
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 #pragma unroll
   for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
-    const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), M - 1);
+    const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), m_end - 1);
     lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
   }
   load_w(0, w0);
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 #pragma unroll
   for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
-    wts[i] = (i < n_l && m0 + (i & 31) < M) ? lv[k] : -INFINITY;
+    wts[i] = (i < n_l && m0 + (i & 31) < m_end) ? lv[k] : -INFINITY;
   }
   for (int i = tid + kLseLoads * kCmbThreads; i < n_l; i += kCmbThreads) {
     const int sp = i >> 5, r = i & 31;
-    wts[i] = (m0 + r < M) ? part_lse[sp * split_stride + (size_t)(m0 + r) * 128 + h] : -INFINITY;
+    wts[i] = (m0 + r < m_end) ? part_lse[sp * split_stride + (size_t)(m0 + r) * 128 + h] : -INFINITY;
   }
   __syncthreads();
   if (tid < 32) {
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 #pragma unroll
     for (int d = 16; d > 0; d >>= 1) last = max(last, __shfl_xor(last, d, 32));
     if (tid == 0) *s_end_lds = last + 1;
-    if (lse_out != nullptr && m < M)
+    if (lse_out != nullptr && m < m_end)
       lse_out[(size_t)m * 128 + h] = (mx != -INFINITY) ? mx + __logf(z) : -INFINITY;
   }
   __syncthreads();
@@ -155,9 +157,10 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   // read across kRowLanes threads) of eight consecutive rows, r0 .. r0+7 with
   // r0 = 8*(tid / kRowLanes) (+8 kGroups in later rounds), so that the
   // partials of eight rows and two splits are in flight together.  A group of
-  // eight rows with none below M is skipped (uniform per row group): its LDS
-  // rows only feed output rows >= M, which are never written.  When the block
-  // has at most eight rows below M, every row group works on them, each on
+  // eight rows with none inside the block (m0 .. m_end-1) is skipped (uniform
+  // per row group): its LDS rows only feed output rows past the block, which
+  // are never written.  When the block has at most eight rows, every row group
+  // works on them, each on
   // every kGroups-th split, and their fp32 sums meet in the (then unused) W_UV
   // staging area.  Splits past the block's last one of non-zero weight are not
   // visited; a split of weight 0 before it (empty: lse = -inf, its partial
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   // the loads of eight rows and two splits in flight together (reading split
   // 0's row in its place, or testing the weight first, measured slower).
   const int cq = tid % kRowLanes, grp = tid / kRowLanes;
-  const bool pair = M - m0 <= 8;                      // uniform over the work-group
+  const bool pair = m_end - m0 <= 8;                      // uniform over the work-group
   float* scratch = reinterpret_cast<float*>(wt);      // [kGroups][8][kOCols] when pair
   auto store_hilo = [&](int r, float4 v) {
     const float ov[4] = {v.x, v.y, v.z, v.w};
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 #pragma unroll 1
     for (int it = 0; it < kIters; ++it) {
       const int r0 = pair ? 0 : grp * 8 + 8 * kGroups * it;
-      if (pair ? it > 0 : m0 + r0 >= M) continue;
+      if (pair ? it > 0 : m0 + r0 >= m_end) continue;
       const int s_first = pair ? grp : 0, s_step = pair ? kGroups : 1;
       const int s_stop = *s_end_lds;
       float4 o[8];
@@ -193,13 +196,13 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
         float4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int m = min(m0 + r0 + u, M - 1);
+          const int m = min(m0 + r0 + u, m_end - 1);
           v[u] = *reinterpret_cast<const float4*>(part_o + (s * split_stride + (size_t)m * 128 + h) * 512 +
                                                   kOCols * p + 4 * cq);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float w = (m0 + r0 + u < M) ? wts[s * 32 + r0 + u] : 0.f;
+          const float w = (m0 + r0 + u < m_end) ? wts[s * 32 + r0 + u] : 0.f;
           const bool use = w != 0.f;
           o[u].x += use ? w * v[u].x : 0.f;
           o[u].y += use ? w * v[u].y : 0.f;
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = m0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (m < M) {
+    if (m < m_end) {
       const __bf16 v = (__bf16)acc[r];
       out[((size_t)m * 128 + h) * 128 + 32 * wave + l32] = __builtin_bit_cast(uint16_t, v);
     }
@@ -330,8 +333,9 @@ extern "C" hipError_t mla_launch_combine(const float* part_o, const float* part_
   // One form per call: a single pass while the grid fits one round of one
   // work-group per compute unit (M <= 64), two passes beyond.
   const int passes = M > 64 ? 2 : 1;
-  const int grid = 128 * ((M + 31) / 32);
-  void* args[] = {&part_o, &part_lse, &w_uv, &out, &lse_out, &M, &S};
+  int rb = M <= 32 ? 16 : 32;
+  const int grid = 128 * ((M + rb - 1) / rb);
+  void* args[] = {&part_o, &part_lse, &w_uv, &out, &lse_out, &M, &S, &rb};
   const void* fn = passes == 2 ? reinterpret_cast<const void*>(&mla::combine_kernel<2>)
                                : reinterpret_cast<const void*>(&mla::combine_kernel<1>);
   return hipLaunchKernel(fn, dim3(grid), dim3(mla::kCmbThreads), args, mla::combine_lds(passes, S), stream);

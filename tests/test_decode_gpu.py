@@ -124,14 +124,16 @@ def test_split_counts(splits):
     _check_decode(make(wl), splits=splits, what=f"splits={splits}")
 
 
-@pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5), (36, 2, 5),
-                                              (67, 1, 40), (33, 3, 41)])
+@pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5), (13, 2, 7),
+                                              (9, 2, 3), (36, 2, 5), (67, 1, 40), (33, 3, 41)])
 def test_combine_row_blocks(batch, tq, splits):
     """The combine's row-block forms.  Single pass (at most 64 rows): 15 rows
     with 40 splits (rows 8-14 past the eight-row pair form), 40 rows with 33
     splits (a full 32-row block, then a block of eight rows that both row groups
     share by split parity) and 9 rows with 5 splits (one row past the pair
-    form).  Two passes (more than 64 rows): 72 rows with 5 splits (a last block
+    form); 16-row blocks (at most 32 rows): 26 rows with 7 splits (a second
+    block of ten rows) and 18 rows with 3 splits (a second block of two rows,
+    shared by split parity).  Two passes (more than 64 rows): 72 rows with 5 splits (a last block
     of eight rows that the four row groups share), 67 rows with 40 splits (the
     most log-sum-exps the first round trip reads; a last block of three rows)
     and 99 rows with 41 splits (one split past it).  Against the absorbed fp64
