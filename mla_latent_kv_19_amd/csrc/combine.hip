@@ -16,7 +16,9 @@
 // transposed reads to form the 8-consecutive-j operand layout.  The split merge
 // skips row groups that lie past M; when a block holds at most eight rows, the
 // row groups of the work-group take alternate splits of the same rows and add
-// their fp32 partial sums in LDS, so few-row decode does not leave them idle.
+// their fp32 partial sums in LDS, so few-row decode does not leave them idle;
+// a block of one row (up to 32 splits) puts all its partials in flight with
+// the log-sum-exps, one round trip for the whole merge.
 //
 // Two forms.  Up to 64 rows (at most 256 work-groups: one round on the chip)
 // the merge covers all 512 latent columns at once (~109 KB of LDS, one
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   // into one) and one thread per row normalises them: one memory round trip
   // for up to 40 splits.  The same threads find the last split of non-zero
   // weight over the block's rows; step 2 stops there.
+  const int cq = tid % kRowLanes, grp = tid / kRowLanes;
   const int n_l = S * 32;
   float lv[kLseLoads];
 #pragma unroll
@@ -114,8 +117,29 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
     const int sp = min(i >> 5, S - 1), m = min(m0 + (i & 31), m_end - 1);
     lv[k] = part_lse[sp * split_stride + (size_t)m * 128 + h];
   }
+  // A block of one row (single pass, at most 32 splits): the partials of all
+  // its splits go in flight here, behind the log-sum-exps and ahead of the
+  // W_UV slices, so that the merge waits one memory round trip instead of one
+  // per two splits.  Thread (grp, cq) takes splits grp, grp + kGroups, ...
+  constexpr int kOneRowLoads = 32 / kGroups;
+  const bool one_row = kPasses == 1 && m_end - m0 == 1 && S <= 32;   // uniform
+  float4 pv[kOneRowLoads];
+  if constexpr (kPasses == 1) {
+    if (one_row) {
+#pragma unroll
+      for (int k = 0; k < kOneRowLoads; ++k) {
+        const int sp = min(grp + kGroups * k, S - 1);
+        pv[k] = *reinterpret_cast<const float4*>(part_o + (sp * split_stride + (size_t)m0 * 128 + h) * 512 + 4 * cq);
+      }
+    }
+  }
   load_w(0, w0);
-  if constexpr (kPasses == 2) load_w(1, w1);
+  if constexpr (kPasses == 2) {
+    load_w(1, w1);
+  } else if (one_row) {
+    load_w(1, w1);
+    load_w(2, w2);
+  }
 #pragma unroll
   for (int k = 0; k < kLseLoads; ++k) {
     const int i = tid + k * kCmbThreads;
@@ -167,7 +191,6 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   // never written) is read and dropped by a select, not a branch, which keeps
   // the loads of eight rows and two splits in flight together (reading split
   // 0's row in its place, or testing the weight first, measured slower).
-  const int cq = tid % kRowLanes, grp = tid / kRowLanes;
   const bool pair = m_end - m0 <= 8;                      // uniform over the work-group
   float* scratch = reinterpret_cast<float*>(wt);      // [kGroups][8][kOCols] when pair
   auto store_hilo = [&](int r, float4 v) {
@@ -191,8 +214,21 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
       float4 o[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (one_row) {
+        // The partials loaded in step 1 (row 0; the other seven stay zero).
+#pragma unroll
+        for (int k = 0; k < kOneRowLoads; ++k) {
+          const int sp = grp + kGroups * k;
+          const float w = (sp < s_stop) ? wts[sp * 32] : 0.f;
+          const bool use = w != 0.f;
+          o[0].x += use ? w * pv[k].x : 0.f;
+          o[0].y += use ? w * pv[k].y : 0.f;
+          o[0].z += use ? w * pv[k].z : 0.f;
+          o[0].w += use ? w * pv[k].w : 0.f;
+        }
+      }
 #pragma unroll 2
-      for (int s = s_first; s < s_stop; s += s_step) {
+      for (int s = one_row ? s_stop : s_first; s < s_stop; s += s_step) {
         float4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -263,8 +299,10 @@ __global__ __launch_bounds__(kCmbThreads) void combine_kernel(
   if constexpr (kPasses == 1) {
     // Slices 0 (since step 1), 1 and 2 in registers, 3 once slice 0 is in LDS.
     merge(0);
-    load_w(1, w1);
-    load_w(2, w2);
+    if (!one_row) {
+      load_w(1, w1);
+      load_w(2, w2);
+    }
     __syncthreads();
     store_w(w0);
     __syncthreads();

@@ -125,7 +125,8 @@ def test_split_counts(splits):
 
 
 @pytest.mark.parametrize("batch,tq,splits", [(5, 3, 40), (20, 2, 33), (9, 1, 5), (13, 2, 7),
-                                              (9, 2, 3), (36, 2, 5), (67, 1, 40), (33, 3, 41)])
+                                              (9, 2, 3), (1, 1, 32), (1, 1, 33), (17, 1, 4),
+                                              (11, 3, 2), (36, 2, 5), (67, 1, 40), (33, 3, 41)])
 def test_combine_row_blocks(batch, tq, splits):
     """The combine's row-block forms.  Single pass (at most 64 rows): 15 rows
     with 40 splits (rows 8-14 past the eight-row pair form), 40 rows with 33
@@ -133,7 +134,10 @@ def test_combine_row_blocks(batch, tq, splits):
     share by split parity) and 9 rows with 5 splits (one row past the pair
     form); 16-row blocks (at most 32 rows): 26 rows with 7 splits (a second
     block of ten rows) and 18 rows with 3 splits (a second block of two rows,
-    shared by split parity).  Two passes (more than 64 rows): 72 rows with 5 splits (a last block
+    shared by split parity).  Blocks of one row, whose partials all load in one
+    round trip up to 32 splits: one row with 32 and with 33 splits (one past:
+    the split-parity loop), 17 rows with 4 (a second 16-row block of one row)
+    and 33 rows with 2 (a second 32-row block of one row).  Two passes (more than 64 rows): 72 rows with 5 splits (a last block
     of eight rows that the four row groups share), 67 rows with 40 splits (the
     most log-sum-exps the first round trip reads; a last block of three rows)
     and 99 rows with 41 splits (one split past it).  Against the absorbed fp64
