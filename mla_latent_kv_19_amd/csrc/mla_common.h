@@ -40,36 +40,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Matrix products whose accumulator must live in VGPRs.
-//
-// The decode kernel keeps 256 fp32 output accumulators per lane in the AGPR
-// file; a second MFMA chain (the scores) has to accumulate in VGPRs, which the
-// compiler will not choose on its own, so that chain is written as inline
-// assembly.  Rules kept by these helpers:
-//  * the chain only ever feeds the same accumulator back as srcC (same opcode,
-//    exact overlap: the hardware forwards it without wait states);
-//  * the operands come from LDS/global loads, whose completion the compiler
-//    already waits for before the asm statement that uses them;
-//  * mfma_vgpr_settle() must follow the chain before any other instruction
-//    touches the accumulator: it inserts 32 wait states, more than the
-//    MFMA-write -> VALU-read requirement of a 32x32x16 product.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ f32x16 mfma32_vgpr_first(bf16x8 a, bf16x8 b) {
-  f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma32_vgpr_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vgpr_settle(f32x16& d) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(d));
-}
-__device__ __forceinline__ void mfma_vgpr_settle2(f32x16& d0, f32x16& d1) {
-  asm volatile("s_nop 15\n\ts_nop 15" : "+v"(d0), "+v"(d1));
-}
-
 // Value-product MFMA accumulating into AGPRs.  Used when every AGPR holds an
 // output accumulator and the compiler's own MFMAs are kept in VGPR form
 // (-mllvm -amdgpu-mfma-vgpr-form for that translation unit).  The compiler
@@ -181,8 +151,6 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Maximum / sum of v over lanes l and l ^ 32 (the two halves of a row of an
 // MFMA 32x32 result), in every lane, with v_permlane32_swap (a VALU exchange,
