@@ -40,18 +40,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Value-product MFMA accumulating into AGPRs.  Used when every AGPR holds an
-// output accumulator and the compiler's own MFMAs are kept in VGPR form
-// (-mllvm -amdgpu-mfma-vgpr-form for that translation unit).  The compiler
-// does not see these as MFMAs, so the callers keep these rules:
+// Value-product MFMAs accumulating into AGPRs, written as inline asm by the
+// decode kernel, where every AGPR holds an output accumulator and the
+// compiler's own MFMAs are kept in VGPR form (-mllvm -amdgpu-mfma-vgpr-form
+// for that translation unit).  The compiler does not see them as MFMAs, so
+// the kernel keeps these rules:
 //  * the B operand written by VALU is passed through valu_to_mfma_settle()
 //    first (VALU write -> MFMA operand read needs wait states);
 //  * every accumulator goes through agpr_settle16() before anything other
 //    than another of these MFMAs reads it, and after a VALU/accvgpr write of
 //    it before the next MFMA reads it (MFMA write -> read: 32 wait states).
-__device__ __forceinline__ void mfma32_agpr(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 __device__ __forceinline__ void valu_to_mfma_settle(bf16x8& b0, bf16x8& b1) {
   asm volatile("s_nop 4" : "+v"(b0), "+v"(b1));
 }
@@ -63,9 +61,7 @@ __device__ __forceinline__ void agpr_settle16(f32x16 (&a)[16]) {
 }
 
 // In-place scaling of one accumulator element held in an AGPR (VALU cannot
-// read AGPRs directly).  agpr_scale_begin/end bracket a run of these with the
-// wait states required around MFMA-written / MFMA-read accumulators.
-__device__ __forceinline__ void agpr_scale_begin() { asm volatile("s_nop 15\n\ts_nop 15"); }
+// read AGPRs directly); a run of these is bracketed by agpr_settle16().
 #define MLA_AGPR_SCALE(elem, factor)                                         \
   do {                                                                       \
     float mla_tmp_;                                                          \
@@ -76,7 +72,6 @@ __device__ __forceinline__ void agpr_scale_begin() { asm volatile("s_nop 15\n\ts
         : "+a"(elem), "=&v"(mla_tmp_)                                        \
         : "v"(factor));                                                      \
   } while (0)
-__device__ __forceinline__ void agpr_scale_end() { asm volatile("s_nop 7"); }
 
 // 16-byte global load reinterpreted as 8 bf16.
 __device__ __forceinline__ bf16x8 ld_global_bf16x8(const uint16_t* p) {
