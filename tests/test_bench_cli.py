@@ -29,3 +29,29 @@ def test_no_gpu_is_an_error_not_a_number():
     assert r.returncode == 2
     assert "needs a GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_traffic_figure_follows_the_decode_machine_code(tmp_path, monkeypatch):
+    """roofline.traffic comes from the committed counters only while the
+    library's decode kernel has the machine code they were taken on: the hash
+    is read from the built library's gfx950 code object (16 hex digits, stable
+    across reads), and a record for other machine code yields None."""
+    sys.path.insert(0, ROOT)
+    import json
+    import bench
+    from mla_latent_kv_19_amd import api
+    lib = api.library_path()
+    if not os.path.exists(lib):
+        pytest.skip("libmla.so not built")
+    h = bench.kernel_code_hash(lib)
+    assert h is not None and len(h) == 16 and int(h, 16) >= 0
+    assert bench.kernel_code_hash(lib) == h
+    assert bench.kernel_code_hash(lib, r"combine_kernel") not in (None, h)
+    rec = {"kernel_code_sha": h, "hbm_bytes_per_launch": 123.0}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic(lib) == 123.0
+    rec["kernel_code_sha"] = "0" * 16 if h != "0" * 16 else "1" * 16
+    f.write_text(json.dumps(rec))
+    assert bench.measured_traffic(lib) is None
